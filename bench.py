@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+One step = one call of moe_fused_forward over one batch: gating, grouping,
+(FP8: activation quantisation), gate/up GEMM + SwiGLU, down GEMM and the
+weighted combine, with every input already resident in HBM.
+
+Default workload: the bf16 decode layer (8 tokens, hidden 4096, 8 experts,
+top-2, SwiGLU intermediate 14336), the shape the headline metric is quoted
+on.  Inputs are seeded synthetic tensors (moe_workloads).
+
+Prints ONE JSON line with tokens/s as `value`, plus:
+  roofline     -- the dominant kernel (the gate/up GEMM): algorithmic bytes
+                  per launch / its average duration, timed with HIP events
+                  recorded around it inside the fused call, against 8 TB/s;
+  cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
+                  the same workload (whole layers, repeated ~10 s).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0}  # dense fp32 / bf16 / fp8
+METRIC = "fused-MoE layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
+DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8"}
+
+
+def hip():
+    h = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def algorithmic(spec, counts):
+    """Bytes / flops the method must move / compute (padding excluded)."""
+    T, H, E, k, I, mode = spec.T, spec.H, spec.E, spec.k, spec.I, spec.mode
+    bw = {0: 4, 1: 2, 2: 1}[mode]
+    bx = 4 if mode == 0 else 2
+    active = int((counts > 0).sum())
+    scale_b = 8 * active if mode == 2 else 0
+    layer_bytes = active * 3 * H * I * bw + scale_b + T * H * bx + 4 * T * E + T * H * bx
+    flops = 6.0 * T * k * H * I
+    w13_bytes = active * 2 * I * H * bw + (4 * active if mode == 2 else 0) + T * H * (
+        1 if mode == 2 else bx) + T * k * I * bx
+    return active, layer_bytes, flops, w13_bytes
+
+
+def cpu_baseline(L, budget_s=10.0):
+    """Time the CPU oracle on whole layers of this workload until ~budget_s."""
+    import oracle
+
+    s = L["spec"]
+    threads = len(os.sched_getaffinity(0))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(s.mode, L["x"], L["logits"], L["w13"], L["w13_scale"], L["w2"],
+                       L["w2_scale"], s.k)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / n * (n + 1) > 3 * budget_s:
+            break
+    omp = os.environ.get("OMP_NUM_THREADS")
+    cores = int(omp) if omp and omp.isdigit() else threads
+    return dict(value=s.T * n / el, unit="tokens/s", cores=min(cores, threads), kind="oracle",
+                sample="%d full layer forward(s) of %s (%d tokens each), %.1f s" % (
+                    n, s.name, s.T, el))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this layer is built and measured on a single "
+              "MI355X (no sharding or collectives); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_layer_gating_amd as moe
+    import moe_workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    spec = wl.WORKLOADS[args.workload]
+    print("bench: generating %s" % spec.name, file=sys.stderr, flush=True)
+    L = wl.make_layer(spec)
+    mode = spec.mode
+
+    def dev_act(a):
+        if mode == 0:
+            return torch.from_numpy(a).cuda()
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    def dev_w(w):
+        if mode == 0:
+            return torch.from_numpy(w).cuda()
+        if mode == 1:
+            return torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(w).cuda()
+
+    x = dev_act(L["x"])
+    logits = torch.from_numpy(L["logits"]).cuda()
+    w13 = dev_w(L["w13"])
+    w2 = dev_w(L["w2"])
+    s13 = None if L["w13_scale"] is None else torch.from_numpy(L["w13_scale"]).cuda()
+    s2 = None if L["w2_scale"] is None else torch.from_numpy(L["w2_scale"]).cuda()
+    shape = moe.make_shape(spec.T, spec.H, spec.E, spec.k, spec.I, mode)
+    ws = moe.workspace(shape)
+    out = torch.empty((spec.T, spec.H), dtype=moe.act_dtype(mode), device="cuda")
+    ids = torch.empty((spec.T, spec.k), dtype=torch.int32, device="cuda")
+
+    def step():
+        moe.moe_fused_forward(x, logits, w13, s13, w2, s2, spec.k, out=out, ws=ws, topk_ids=ids)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=spec.E)
+
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+
+    # dominant kernel: HIP events recorded around each stage inside the fused call
+    H_ = hip()
+    evs = []
+    for _ in range(moe.NUM_STAGE_EVENTS):
+        e = ctypes.c_void_p()
+        assert H_.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    reps = max(args.steps, 10)
+    stage_ms = np.zeros(moe.NUM_STAGE_EVENTS - 1)
+    for _ in range(reps):
+        moe.moe_fused_forward_events(x, logits, w13, s13, w2, s2, spec.k, evs, out=out, ws=ws,
+                                     topk_ids=ids)
+        H_.hipEventSynchronize(ctypes.c_void_p(evs[-1]))
+        for i in range(moe.NUM_STAGE_EVENTS - 1):
+            f = ctypes.c_float()
+            H_.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(evs[i]),
+                                   ctypes.c_void_p(evs[i + 1]))
+            stage_ms[i] += f.value
+    stage_ms /= reps
+    for e in evs:
+        H_.hipEventDestroy(ctypes.c_void_p(e))
+    active, layer_bytes, flops, w13_bytes = algorithmic(spec, counts)
+    w13_ms = stage_ms[4]
+    w13_gbs = w13_bytes / (w13_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(L)
+
+    rec = {
+        "metric": METRIC,
+        "value": spec.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[mode],
+        "data": "synthetic (seeded, moe_workloads recipe)",
+        "config": {"workload": "%s: T=%d H=%d E=%d k=%d I=%d" % (
+            spec.name, spec.T, spec.H, spec.E, spec.k, spec.I), "T": spec.T, "H": spec.H,
+            "E": spec.E, "k": spec.k, "I": spec.I, "active_experts": active},
+        "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_tflops": flops / (ms * 1e-3) / 1e12,
+        "stage_ms": {n: round(float(v), 5) for n, v in zip(
+            ["gating", "align_sort", "tiles", "x_quant", "w13_swiglu", "h_quant", "w2",
+             "combine"], stage_ms)},
+        "roofline": {"bound": "hbm", "kernel": "w13_swiglu_skinny", "achieved": w13_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": w13_bytes, "avg_ms": float(w13_ms)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * moe_gfx950.h -- C ABI of the fused Mixture-of-Experts layer for AMD MI355X
+ * (gfx950).
+ *
+ * The layer is the fused MoE operation: token routing, data shuffling into
+ * expert order, the expert network and the weighted aggregation of expert
+ * outputs, run as one batched GPU operation (readmex.ai, "AWS details fused
+ * MoE kernel optimizations on SageMaker, up to 10% throughput gain", summary;
+ * agentic-affairs.com, "Swap-AB targets matrix execution on Hopper").  The
+ * FP8 mode folds the tensor scales into the matrix pass and aggregates the
+ * expert outputs in the same pipeline (codebridge-ai.com,
+ * "aws-moe-kernel-wgmma-triton-ttft", section "2. Backend routing";
+ * agentic-affairs.com, "Triton improves the FP8 execution path").
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise; `moe_shape` is a
+ *    host struct.  The caller owns every buffer.  The library never allocates
+ *    or frees memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work; nothing synchronises the host.  Outputs are
+ *    ready when the stream reaches them.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    failed check returns a negative moe_status and leaves every buffer
+ *    untouched.  A launch failure returns MOE_ERR_HIP.  T = 0 (with otherwise
+ *    valid sizes) returns MOE_OK at once: no buffer is checked or touched.
+ *  - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 16), 0 <= T, T*k < 2^31,
+ *    H and I positive multiples of 128 (MOE_ERR_UNSUPPORTED otherwise),
+ *    every device pointer 16-byte aligned.
+ *  - Preconditions the device does not check (violations are undefined):
+ *    logits hold no NaN and at least k non-(-inf) entries per row;
+ *    topk_ids lie in [0, E); sorted_ids / expert_offsets / inv_perm are the
+ *    outputs of moe_align_sort for the same ids.
+ *  - Results are deterministic: routing outputs are bit-identical run to run
+ *    and floating-point outputs do not depend on scheduling (no floating
+ *    atomics; maxima use integer atomics, which are order-free).
+ *
+ * Data types by mode (moe_shape.wdtype):
+ *   MOE_F32      : x, h, out fp32; w13, w2 fp32; no scales.
+ *   MOE_BF16     : x, h, out bf16; w13, w2 bf16; no scales.
+ *   MOE_FP8_E4M3 : x, h, out bf16; w13, w2 OCP e4m3fn codes with one fp32
+ *                  dequantisation scale per expert and matrix; x and h are
+ *                  quantised to e4m3 inside the layer with dynamic
+ *                  per-tensor scales (amax / 448).
+ * Layouts (row-major, last index contiguous):
+ *   x [T,H]; logits [T,E] fp32; w13 [E,2I,H] (rows 0..I-1 gate, I..2I-1 up);
+ *   w2 [E,H,I]; h [T*k,I] and y [T*k,H] in expert-sorted pair order;
+ *   out [T,H]; topk_ids / topk_weights [T,k]; a pair (t,j) has flat index
+ *   f = t*k + j.
+ */
+#ifndef MOE_GFX950_H
+#define MOE_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad T, E, k, dtype */
+  MOE_ERR_UNSUPPORTED = -2, /* H or I not a multiple of 128 */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4          /* a kernel launch failed */
+} moe_status;
+
+/* Layer shape (host struct).  renormalize: 1 = top-k softmax renormalised
+ * over the selected experts, 0 = plain softmax probabilities. */
+typedef struct {
+  int32_t T, H, E, k, I;
+  int32_t wdtype;
+  int32_t renormalize;
+} moe_shape;
+
+/* Host only.  Checks a shape against the limits above; returns a moe_status. */
+int moe_check_shape(const moe_shape* s);
+
+/* Host only.  Bytes of device workspace that every entry point of this
+ * shape may use (the fused entry point needs the most).  Returns 0 for an
+ * invalid shape.  The workspace must be 256-byte aligned. */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/* Host only.  Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* Top-k softmax gating (token routing).
+ * logits [T,E] fp32 in; topk_ids [T,k] int32 and topk_weights [T,k] fp32 out.
+ * Slot j holds the expert with the (j+1)-th largest logit; equal logits go
+ * to the lower expert index; -0 equals +0.  Weights: exp(l - l_max) over
+ * the selected experts divided by their sum (renormalize = 1) or by the sum
+ * over all experts (renormalize = 0). */
+int moe_topk_gating(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                    int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Grouping of pairs by expert ("data shuffling").
+ * expert_counts[e] = number of pairs routed to e; expert_offsets = exclusive
+ * prefix sum of the counts ([E+1], offsets[E] = T*k); sorted_ids [T*k] lists
+ * the flat pair indices by expert ascending and, inside an expert, by pair
+ * index ascending; inv_perm [T*k] (may be NULL) is its inverse. */
+int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                   int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                   int32_t* inv_perm, void* stream);
+
+/* Expert gate/up projection with SwiGLU, grouped over experts.
+ * For sorted position p (pair f = sorted_ids[p], token t = f / k, expert e
+ * with offsets[e] <= p < offsets[e+1]):
+ *   g_n = x[t] . w13[e][n],  u_n = x[t] . w13[e][I+n]    (fp32 accumulation)
+ *   FP8: x is first quantised per tensor (codes e4m3(x * 448/amax(x))), the
+ *        products use the codes and both sums are scaled by
+ *        fl32(s_x * w13_scale[e]), s_x = amax(x)/448.
+ *   h[p][n] = silu(g_n) * u_n, stored in the activation type.
+ * act_scales [4] fp32 out (FP8 mode; left untouched otherwise):
+ *   {s_x, s_h, amax(x), amax(h)} with s_h = amax(h)/448 (amax = 0 -> scale 1).
+ * w13_scale [E] is required in FP8 mode and ignored otherwise. */
+int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w13,
+                                const float* w13_scale, const int32_t* sorted_ids,
+                                const int32_t* expert_offsets, void* h, float* act_scales,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Expert down projection, grouped over experts, unweighted.
+ *   y[p][m] = h[p] . w2[e][m] (fp32 accumulation), e the expert of position p.
+ *   FP8: h is quantised per tensor with the scale derived from
+ *        act_scales[3] = amax(h) (codes e4m3(h * 448/amax)), and y is scaled
+ *        by fl32(s_h * w2_scale[e]).
+ * y [T*k,H] fp32 out, sorted order. */
+int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const float* w2_scale,
+                        const int32_t* expert_offsets, const float* act_scales, float* y,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted aggregation: out[t][m] = sum_{j<k} topk_weights[t][j] *
+ * y[inv_perm[t*k+j]][m], summed in fp32 in slot order and rounded once to
+ * the activation type. */
+int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
+                const float* topk_weights, void* out, void* stream);
+
+/* The whole layer in one call: gating, grouping, (FP8: x quantisation),
+ * gate/up + SwiGLU, (FP8: h quantisation), down projection and aggregation,
+ * enqueued back to back on `stream`.  Every token row of `out` is written
+ * exactly once.  topk_ids / topk_weights are optional outputs (NULL = kept
+ * in the workspace). */
+int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, const void* w13,
+                      const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+                      int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Stage timing for profiling: identical to moe_fused_forward, and in
+ * addition records events[i] (each a hipEvent_t created by the caller) on
+ * `stream` at stage boundary i, so that the elapsed time between
+ * consecutive events is the time of one stage:
+ *   0 before gating | 1 after gating | 2 after grouping | 3 after the tile
+ *   list | 4 after x quantisation (FP8; else same point as 3) | 5 after the
+ *   gate/up GEMM | 6 after h quantisation (FP8; else same as 5) | 7 after
+ *   the down GEMM | 8 after the aggregation.
+ * n_events must be MOE_NUM_STAGE_EVENTS. */
+#define MOE_NUM_STAGE_EVENTS 9
+int moe_fused_forward_events(const moe_shape* s, const void* x, const float* logits,
+                             const void* w13, const float* w13_scale, const void* w2,
+                             const float* w2_scale, void* out, int32_t* topk_ids,
+                             float* topk_weights, void* ws, size_t ws_bytes, void* stream,
+                             void** events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_GFX950_H */

@@ -1,0 +1,339 @@
+// api.cpp -- host side of the fused MoE library: argument checks, workspace
+// carve-up and the launch sequences behind the C ABI in include/moe_gfx950.h.
+//
+// Nothing here is specialised on the token count or on the per-expert
+// counts: they are runtime values read by the kernels on the device, so a
+// new batch size never triggers a rebuild (the lesson of codebridge-ai.com,
+// "aws-moe-kernel-wgmma-triton-ttft", section "3. Kill JIT recompilation",
+// applied to an ahead-of-time library).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "moe_common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kSkinnyBM = 16;  // sorted positions per GEMM tile (MFMA column width)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int act_bytes(int wdtype) { return wdtype == MOE_F32 ? 4 : 2; }
+
+inline int w_bytes(int wdtype) {
+  return wdtype == MOE_F32 ? 4 : (wdtype == MOE_BF16 ? 2 : 1);
+}
+
+inline long max_tiles_for(long n_pairs, int E, int bm) {
+  long nz = n_pairs < E ? n_pairs : E;  // experts that can be non-empty
+  return n_pairs / bm + nz;
+}
+
+// Offsets of the workspace regions for one shape.
+struct Layout {
+  size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, xq, hq, h, y, total;
+  long max_tiles;
+};
+
+Layout layout_for(const moe_shape& s) {
+  Layout L;
+  const long np = (long)s.T * s.k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.max_tiles = max_tiles_for(np, s.E, kSkinnyBM);
+  L.ctrl = take(sizeof(Ctrl));
+  L.ids = take(np * 4);
+  L.wts = take(np * 4);
+  L.counts = take((size_t)s.E * 4);
+  L.offsets = take((size_t)(s.E + 1) * 4);
+  L.sorted = take(np * 4);
+  L.inv = take(np * 4);
+  L.tiles = take((size_t)(L.max_tiles + 1) * sizeof(Tile));
+  const bool fp8 = s.wdtype == MOE_FP8_E4M3;
+  L.xq = take(fp8 ? (size_t)s.T * s.H : 0);
+  L.hq = take(fp8 ? (size_t)np * s.I : 0);
+  L.h = take((size_t)np * s.I * act_bytes(s.wdtype));
+  L.y = take((size_t)np * s.H * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+int check_common(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_ERR_INVALID_ARG;
+  if ((long)T * k >= (1L << 31)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_ws(const moe_shape* s, void* ws, size_t ws_bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_workspace_bytes(s)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// Enqueue: per-tensor e4m3 quantisation of a bf16 tensor (amax, then codes).
+int enqueue_quant(const uint16_t* src, long n, uint32_t* amax_bits, uint8_t* dst, hipStream_t st) {
+  MOE_TRY(launch_amax_bf16(src, n, amax_bits, st));
+  MOE_TRY(launch_quant_e4m3(src, n, amax_bits, dst, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  int rc = check_common(s->T, s->E, s->k);
+  if (rc) return rc;
+  if (s->wdtype < MOE_F32 || s->wdtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (s->H <= 0 || s->I <= 0) return MOE_ERR_INVALID_ARG;
+  if (s->H % 128 || s->I % 128) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (moe_check_shape(s) != MOE_OK) return 0;
+  return layout_for(*s).total;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (H and I must be multiples of 128)";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int moe_topk_gating(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                    int32_t* topk_ids, float* topk_weights, void* stream) {
+  int rc = check_common(T, E, k);
+  if (rc) return rc;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_weights))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(
+      launch_topk_gating(logits, T, E, k, renormalize, topk_ids, topk_weights, nullptr, 0, st));
+}
+
+int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                   int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                   int32_t* inv_perm, void* stream) {
+  int rc = check_common(T, E, k);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !expert_counts || !expert_offsets || !sorted_ids) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
+      !aligned16(sorted_ids) || (inv_perm && !aligned16(inv_perm)))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(launch_align_sort(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_ids,
+                                      inv_perm, st));
+}
+
+int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w13,
+                                const float* w13_scale, const int32_t* sorted_ids,
+                                const int32_t* expert_offsets, void* h, float* act_scales,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  const bool fp8 = s->wdtype == MOE_FP8_E4M3;
+  if (!x || !w13 || !sorted_ids || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!w13_scale || !act_scales)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(sorted_ids) || !aligned16(expert_offsets) ||
+      !aligned16(h) || (fp8 && (!aligned16(w13_scale) || !aligned16(act_scales))))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Layout L = layout_for(*s);
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  Tile* tiles = at<Tile>(ws, L.tiles);
+  MOE_TRY(launch_zero_words(reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
+  MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, ctrl, st));
+  const void* b = x;
+  if (fp8) {
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    if ((rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)s->T * s->H,
+                            &ctrl->amax_x_bits, xq, st)))
+      return rc;
+    b = xq;
+  }
+  MOE_TRY(launch_w13_swiglu(s->wdtype, b, w13, w13_scale, sorted_ids, tiles, ctrl, (int)L.max_tiles,
+                            s->H, s->I, s->k, &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+  if (fp8) MOE_TRY(launch_write_scales(ctrl, act_scales, st));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const float* w2_scale,
+                        const int32_t* expert_offsets, const float* act_scales, float* y,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  const bool fp8 = s->wdtype == MOE_FP8_E4M3;
+  if (!h || !w2 || !expert_offsets || !y) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!w2_scale || !act_scales)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(expert_offsets) || !aligned16(y) ||
+      (fp8 && (!aligned16(w2_scale) || !aligned16(act_scales))))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Layout L = layout_for(*s);
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  Tile* tiles = at<Tile>(ws, L.tiles);
+  MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, ctrl, st));
+  const void* b = h;
+  // act_scales[3] holds amax(h) as an fp32 value; its bit pattern is what the
+  // kernels read.
+  const uint32_t* amax_h = reinterpret_cast<const uint32_t*>(fp8 ? act_scales + 3 : nullptr);
+  if (fp8) {
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    MOE_TRY(launch_quant_e4m3(reinterpret_cast<const uint16_t*>(h), (long)s->T * s->k * s->I,
+                              amax_h, hq, st));
+    b = hq;
+  }
+  MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I, amax_h,
+                    y, st));
+  return MOE_OK;
+}
+
+int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
+                const float* topk_weights, void* out, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!y || !inv_perm || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y) || !aligned16(inv_perm) || !aligned16(topk_weights) || !aligned16(out))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(
+      launch_combine(s->wdtype, y, inv_perm, topk_weights, s->T, s->H, s->k, out, st));
+}
+
+}  // extern "C"
+
+namespace {
+
+int fused_impl(const moe_shape* s, const void* x, const float* logits, const void* w13,
+               const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+               int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream,
+               void** events) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  const bool fp8 = s->wdtype == MOE_FP8_E4M3;
+  if (!x || !logits || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!w13_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(logits) || !aligned16(w13) || !aligned16(w2) ||
+      !aligned16(out) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_weights && !aligned16(topk_weights)) ||
+      (fp8 && (!aligned16(w13_scale) || !aligned16(w2_scale))))
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) : hipSuccess;
+  };
+  const Layout L = layout_for(*s);
+  const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I;
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* wts = topk_weights ? topk_weights : at<float>(ws, L.wts);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  Tile* tiles = at<Tile>(ws, L.tiles);
+  void* h = at<void>(ws, L.h);
+  float* y = at<float>(ws, L.y);
+
+  MOE_TRY(mark(0));
+  MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
+                             reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
+  MOE_TRY(mark(1));
+  MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
+  MOE_TRY(mark(2));
+  MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, ctrl, st));
+  MOE_TRY(mark(3));
+  const void* bx = x;
+  if (fp8) {
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    if ((rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,
+                            xq, st)))
+      return rc;
+    bx = xq;
+  }
+  MOE_TRY(mark(4));
+  MOE_TRY(launch_w13_swiglu(s->wdtype, bx, w13, w13_scale, sorted, tiles, ctrl, (int)L.max_tiles, H,
+                            I, k, &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+  MOE_TRY(mark(5));
+  const void* bh = h;
+  if (fp8) {
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    MOE_TRY(launch_quant_e4m3(reinterpret_cast<const uint16_t*>(h), (long)T * k * I,
+                              &ctrl->amax_h_bits, hq, st));
+    bh = hq;
+  }
+  MOE_TRY(mark(6));
+  MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,
+                    &ctrl->amax_h_bits, y, st));
+  MOE_TRY(mark(7));
+  MOE_TRY(launch_combine(s->wdtype, y, inv, wts, T, H, k, out, st));
+  MOE_TRY(mark(8));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, const void* w13,
+                      const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+                      int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return fused_impl(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
+                    ws_bytes, stream, nullptr);
+}
+
+int moe_fused_forward_events(const moe_shape* s, const void* x, const float* logits,
+                             const void* w13, const float* w13_scale, const void* w2,
+                             const float* w2_scale, void* out, int32_t* topk_ids,
+                             float* topk_weights, void* ws, size_t ws_bytes, void* stream,
+                             void** events, int32_t n_events) {
+  if (!events || n_events != MOE_NUM_STAGE_EVENTS) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; i++)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return fused_impl(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
+                    ws_bytes, stream, events);
+}
+
+}  // extern "C"

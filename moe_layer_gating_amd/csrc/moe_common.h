@@ -1,0 +1,105 @@
+// moe_common.h -- device helpers and internal launcher declarations shared by
+// the HIP translation units of the fused MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_gfx950.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One unit of grouped-GEMM work: `mt` consecutive sorted positions starting
+// at `p0`, all routed to expert `e`.
+struct Tile {
+  int32_t e, p0, mt, pad;
+};
+
+// Control words at the start of the workspace (zeroed at the start of a call
+// by the first kernel that runs).
+struct Ctrl {
+  uint32_t amax_x_bits;  // max |x| as fp32 bits (non-negative floats order as uints)
+  uint32_t amax_h_bits;  // max |h| as fp32 bits
+  int32_t num_tiles;     // tiles written by the tile builder
+  int32_t pad[61];
+};
+static_assert(sizeof(Ctrl) == 256, "ctrl block is one 256-byte slot");
+
+// ----------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating to +-448.
+// Normal range: drop 20 fraction bits of the fp32 pattern with a
+// nearest-even carry (the carry may bump the exponent) and rebias 127 -> 7.
+// Below 2^-6: the value is an integer multiple of 2^-9 after rounding.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(v);
+  if (!(a <= 448.0f)) return (a != a) ? (sign | 0x7fu) : (sign | 0x7eu);
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  uint32_t x = u & 0x7fffffffu;
+  x += 0x7ffffu + ((x >> 20) & 1u);
+  return sign | ((x >> 20) - (120u << 3));
+}
+
+// ----------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// --------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All work goes to `st`.
+hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st);
+hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
+                             hipStream_t st);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles, Ctrl* ctrl,
+                              hipStream_t st);
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
+hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hipStream_t st);
+hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_bits, uint8_t* dst,
+                             hipStream_t st);
+hipError_t launch_write_scales(const Ctrl* ctrl, float* act_scales, hipStream_t st);
+// Grouped GEMMs.  `b` is the token-side operand: x (fp32/bf16) or the e4m3
+// codes of x (FP8) for w13; h (fp32/bf16) or the codes of h (FP8) for w2.
+// `act_amax_bits` (FP8 only) points at amax of that activation as fp32 bits.
+hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const float* w13_scale,
+                             const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl,
+                             int max_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
+                             void* h, uint32_t* amax_h_bits, hipStream_t st);
+hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
+                     const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
+                     const uint32_t* act_amax_bits, float* y, hipStream_t st);
+hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,
+                          int H, int k, void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,267 @@
+// route.hip -- token routing and grouping kernels of the fused MoE layer.
+//
+// Routing (top-k softmax gating) and the regrouping of (token, slot) pairs into
+// expert-contiguous order are the "token routing" and "data shuffling" stages
+// of the fused MoE operation (readmex.ai, "AWS details fused MoE kernel
+// optimizations on SageMaker, up to 10% throughput gain", summary).  Both stay
+// on the device so that no host round-trip sits between them and the expert
+// GEMMs (explore.n1n.ai, "Mixture-of-Experts Kernel Engineering on Amazon
+// SageMaker AI", section "2. Triton Backend Routing for FP8 Quantization").
+// Per-expert batch sizes are data dependent (same page, "The Core
+// Bottlenecks of MoE Inference on H200 GPUs"): they are produced here as
+// counts / offsets / a tile list that the GEMMs read on the device, so no
+// kernel is specialised on them.
+#include "moe_common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- gating
+// One wave per token.  Lane l holds logits e = l, l+64, ... (up to 16 each).
+// k rounds of a wave-wide arg-max over the experts not yet taken; the order
+// is (logit descending, expert index ascending).  Float comparison makes
+// -0 == +0.  After round j, lane j keeps the winner, so lanes 0..k-1 end up
+// holding slot j's (value, expert).
+constexpr int kMaxPerLane = 16;  // E <= 1024
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int k, int renorm,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ wts,
+                                                          uint32_t* zero_words, int n_zero) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_zero) zero_words[threadIdx.x] = 0u;
+  const int lane = lane_id();
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[kMaxPerLane];
+  const int per_lane = (E + kWave - 1) / kWave;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; i++) {
+    int e = lane + i * kWave;
+    v[i] = (i < per_lane && e < E) ? row[e] : -INFINITY;
+  }
+  uint32_t taken = 0;  // bit i: slot i of this lane already selected (or absent)
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; i++)
+    if (!(i < per_lane && lane + i * kWave < E)) taken |= 1u << i;
+
+  float my_v = -INFINITY, top_v = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; j++) {
+    // best untaken candidate of this lane
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; i++) {
+      int e = lane + i * kWave;
+      if (!(taken & (1u << i)) && better(v[i], e, bv, be)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    // butterfly arg-max: every lane ends with the wave winner
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o);
+      int oe = __shfl_xor(be, o);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be < E && (be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+    if (j == 0) top_v = bv;
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  // weights: exp(l - l_top) over the selected slots, divided by their sum
+  // (renorm) or by the sum over every expert (top_v is the row maximum).
+  float ex = (lane < k) ? expf(my_v - top_v) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = wave_sum(ex);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; i++)
+      if (i < per_lane && lane + i * kWave < E) s += expf(v[i] - top_v);
+    denom = wave_sum(s);
+  }
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_e;
+    wts[(size_t)t * k + lane] = ex / denom;
+  }
+}
+
+hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st) {
+  const int tokens_per_block = 4;
+  int grid = (T + tokens_per_block - 1) / tokens_per_block;
+  if (grid < 1) grid = 1;
+  topk_gating_kernel<<<grid, 256, 0, st>>>(logits, T, E, k, renorm, ids, w, zero_words, n_zero);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ block scans
+// Exclusive scan of one int per thread over a 256-thread block; returns the
+// prefix and writes the block total to *total.  `tmp` holds 4 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* tmp, int* total) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    int c = tmp[i];
+    if (i < w) base += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// -------------------------------------------------------------- align sort
+// grid = E blocks of 256 threads.  Every block builds the full expert
+// histogram in LDS (integer atomics: the counts do not depend on order) and
+// its exclusive scan, then block e gathers the pairs routed to expert e in
+// ascending pair order with a ballot-based stable compaction.  No atomic
+// decides a position, so the permutation is the same on every run.
+__global__ __launch_bounds__(256) void align_sort_kernel(const int32_t* __restrict__ ids, int n,
+                                                         int E, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_ids,
+                                                         int32_t* __restrict__ inv_perm) {
+  __shared__ int hist[1024];
+  __shared__ int tmp[4];
+  const int e = blockIdx.x;
+  for (int i = threadIdx.x; i < E; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int f = threadIdx.x; f < n; f += 256) atomicAdd(&hist[ids[f]], 1);
+  __syncthreads();
+  // exclusive scan over E (<= 1024): thread i owns entries 4i .. 4i+3
+  int local[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    int idx = threadIdx.x * 4 + q;
+    local[q] = (idx < E) ? hist[idx] : 0;
+    s += local[q];
+  }
+  int total;
+  int pre = block_exclusive_scan_256(s, tmp, &total);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    int idx = threadIdx.x * 4 + q;
+    if (idx < E) hist[idx] = pre;  // hist now holds the exclusive offsets
+    pre += local[q];
+  }
+  __syncthreads();
+  const int base = hist[e];
+  const int cnt = (e + 1 < E ? hist[e + 1] : n) - base;
+  if (threadIdx.x == 0) {
+    counts[e] = cnt;
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = n;
+  }
+  if (cnt == 0) return;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int running = 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    int f = c0 + threadIdx.x;
+    bool flag = (f < n) && ids[f] == e;
+    uint64_t m = __ballot(flag);
+    int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) tmp[w] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int cw = tmp[i];
+      if (i < w) before += cw;
+      tot += cw;
+    }
+    if (flag) {
+      int pos = base + running + before + rank;
+      sorted_ids[pos] = f;
+      if (inv_perm) inv_perm[f] = pos;
+    }
+    running += tot;
+    __syncthreads();
+    if (running == cnt) break;  // uniform across the block
+  }
+}
+
+hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
+                             hipStream_t st) {
+  align_sort_kernel<<<E, 256, 0, st>>>(ids, T * k, E, counts, offsets, sorted_ids, inv_perm);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- tile list
+// One block of 256 threads.  Expert e with c = offsets[e+1]-offsets[e] pairs
+// contributes ceil(c / bm) tiles of at most bm consecutive sorted positions;
+// tiles are listed expert by expert.  The tile count goes to ctrl->num_tiles.
+__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
+                                                          int bm, Tile* __restrict__ tiles,
+                                                          Ctrl* ctrl) {
+  __shared__ int tmp[4];
+  int local[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    int e = threadIdx.x * 4 + q;
+    int c = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    local[q] = (c + bm - 1) / bm;
+    s += local[q];
+  }
+  int total;
+  int pre = block_exclusive_scan_256(s, tmp, &total);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    int e = threadIdx.x * 4 + q;
+    if (e < E) {
+      int p = offsets[e], end = offsets[e + 1];
+      for (int i = 0; i < local[q]; i++) {
+        Tile tl;
+        tl.e = e;
+        tl.p0 = p + i * bm;
+        tl.mt = min(bm, end - tl.p0);
+        tl.pad = 0;
+        tiles[pre + i] = tl;
+      }
+    }
+    pre += local[q];
+  }
+  if (threadIdx.x == 0) ctrl->num_tiles = total;
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles, Ctrl* ctrl,
+                              hipStream_t st) {
+  build_tiles_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tiles, ctrl);
+  return hipGetLastError();
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
+  zero_words_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,76 @@
+"""Helpers shared by the GPU tests: upload seeded layers, compare results.
+
+Inputs come from moe_workloads (seeded); expected values come from the CPU
+oracle only.  Nothing here computes the layer itself.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import moe_layer_gating_amd as moe
+import oracle
+
+F32, BF16, FP8 = 0, 1, 2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def act_to_torch(a, mode, dev="cuda"):
+    if mode == F32:
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+
+
+def w_to_torch(w, mode, dev="cuda"):
+    if mode == F32:
+        return torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(dev)
+    if mode == BF16:
+        return torch.from_numpy(np.ascontiguousarray(w, np.uint16).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(w, np.uint8)).to(dev)
+
+
+def act_to_numpy(t, mode):
+    t = t.detach().cpu().contiguous()
+    if mode == F32:
+        return t.numpy().astype(np.float32)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def upload(layer, dev="cuda"):
+    s = layer["spec"]
+    d = dict(
+        x=act_to_torch(layer["x"], s.mode, dev),
+        logits=torch.from_numpy(layer["logits"]).to(dev),
+        w13=w_to_torch(layer["w13"], s.mode, dev),
+        w2=w_to_torch(layer["w2"], s.mode, dev),
+        w13_scale=None if layer["w13_scale"] is None else torch.from_numpy(layer["w13_scale"]).to(dev),
+        w2_scale=None if layer["w2_scale"] is None else torch.from_numpy(layer["w2_scale"]).to(dev),
+    )
+    return d
+
+
+def rel_inf(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0)) if ref.size else 0.0
+
+
+# tolerance on the layer output, max |gpu - ref| / max |ref|
+OUT_TOL = {F32: 1e-5, BF16: 5e-3, FP8: 2e-2}
+
+
+def int_tensor(a, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+
+def f32_tensor(a, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)

@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports every function the header declares,
+and its host-side checks reject bad arguments before anything is enqueued.
+CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_layer_gating_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_gfx950.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        import moe_layer_gating_amd._build as b
+
+        b.build()
+    return moe.lib()
+
+
+def test_header_declares_the_six_entry_points():
+    names = _declared_functions()
+    for n in ("moe_topk_gating", "moe_align_sort", "moe_grouped_gemm_w13_swiglu",
+              "moe_grouped_gemm_w2", "moe_combine", "moe_fused_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert name in moe.EXPORTS
+
+
+def test_status_strings(L):
+    for rc in (0, -1, -2, -3, -4):
+        assert L.moe_status_string(rc)
+    assert L.moe_status_string(-99) == b"unknown status"
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((16, 128, 8, 2, 256, 0), 0),
+    ((8, 4096, 8, 2, 14336, 1), 0),
+    ((4096, 7168, 256, 8, 2048, 2), 0),
+    ((0, 128, 8, 2, 256, 2), 0),          # T = 0 is valid (a no-op)
+    ((-1, 128, 8, 2, 256, 0), -1),
+    ((4, 128, 0, 1, 256, 0), -1),         # E = 0
+    ((4, 128, 1025, 2, 256, 0), -1),      # E > 1024
+    ((4, 128, 8, 0, 256, 0), -1),         # k = 0
+    ((4, 128, 8, 9, 256, 0), -1),         # k > E
+    ((4, 128, 32, 17, 256, 0), -1),       # k > 16
+    ((4, 128, 8, 2, 256, 3), -1),         # bad dtype
+    ((4, 100, 8, 2, 256, 0), -2),         # H not a multiple of 128
+    ((4, 128, 8, 2, 200, 1), -2),         # I not a multiple of 128
+])
+def test_check_shape(L, shape, want):
+    T, H, E, k, I, dt = shape
+    s = moe.make_shape(T, H, E, k, I, dt)
+    assert moe.moe_check_shape(s) == want
+    ws = moe.moe_workspace_bytes(s)
+    assert (ws > 0) == (want == 0)
+
+
+def test_workspace_grows_with_tokens(L):
+    a = moe.moe_workspace_bytes(moe.make_shape(1, 4096, 64, 8, 8192, 2))
+    b = moe.moe_workspace_bytes(moe.make_shape(16, 4096, 64, 8, 8192, 2))
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_invalid_pointers_rejected_before_launch(L):
+    good = _fake(0x100000)
+    odd = _fake(0x100004)  # 4-byte aligned only
+    # gating: null / misaligned / bad k
+    assert L.moe_topk_gating(None, 4, 8, 2, 1, good, good, None) == -1
+    assert L.moe_topk_gating(odd, 4, 8, 2, 1, good, good, None) == -1
+    assert L.moe_topk_gating(good, 4, 8, 9, 1, good, good, None) == -1
+    assert L.moe_topk_gating(good, 4, 8, 2, 2, good, good, None) == -1
+    assert L.moe_topk_gating(good, 0, 8, 2, 1, good, good, None) == 0  # T = 0: nothing enqueued
+    # align sort
+    assert L.moe_align_sort(good, 4, 2, 8, None, good, good, None, None) == -1
+    assert L.moe_align_sort(good, 4, 2, 8, good, good, odd, None, None) == -1
+    assert L.moe_align_sort(good, 0, 2, 8, good, good, good, None, None) == 0
+    s = moe.make_shape(4, 256, 8, 2, 256, 2)
+    S = ctypes.byref(s)
+    need = moe.moe_workspace_bytes(s)
+    ws = _fake(0x200000)
+    # FP8 needs scales
+    assert L.moe_grouped_gemm_w13_swiglu(S, good, good, None, good, good, good, good, ws, need,
+                                         None) == -1
+    # workspace too small / misaligned
+    assert L.moe_grouped_gemm_w13_swiglu(S, good, good, good, good, good, good, good, ws, need - 1,
+                                         None) == -3
+    assert L.moe_grouped_gemm_w13_swiglu(S, good, good, good, good, good, good, good,
+                                         _fake(0x200010), need, None) == -3
+    assert L.moe_grouped_gemm_w2(S, good, good, None, good, good, good, ws, need, None) == -1
+    assert L.moe_combine(S, good, good, None, good, None) == -1
+    assert L.moe_fused_forward(S, good, good, good, good, good, None, good, None, None, ws, need,
+                               None) == -1
+    s2 = moe.make_shape(4, 200, 8, 2, 256, 1)
+    assert L.moe_fused_forward(ctypes.byref(s2), good, good, good, None, good, None, good, None,
+                               None, ws, 1 << 30, None) == -2
+    s0 = moe.make_shape(0, 256, 8, 2, 256, 2)
+    assert L.moe_fused_forward(ctypes.byref(s0), good, good, good, good, good, good, good, None,
+                               None, ws, moe.moe_workspace_bytes(s0), None) == 0
