@@ -17,8 +17,6 @@ using namespace moe;
 
 namespace {
 
-constexpr int kSkinnyBM = 16;  // sorted positions per GEMM tile (MFMA column width)
-
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -36,9 +34,16 @@ inline long max_tiles_for(long n_pairs, int E, int bm) {
 
 // Offsets of the workspace regions for one shape.
 struct Layout {
-  size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, xq, hq, h, y, total;
-  long max_tiles;
+  size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, tiles_big, xq, hq, h, y, total;
+  long max_tiles, max_tiles_big;
 };
+
+// Shape class: the many-token tiled GEMMs once experts receive 16 or more
+// pairs on average (bf16 and FP8); the few-token swap-AB GEMMs otherwise.
+// Decided from the shape alone, so no per-call specialisation arises.
+inline bool use_tiles(const moe_shape& s) {
+  return s.wdtype != MOE_F32 && (long)s.T * s.k >= 16L * s.E;
+}
 
 Layout layout_for(const moe_shape& s) {
   Layout L;
@@ -50,6 +55,7 @@ Layout layout_for(const moe_shape& s) {
     return at;
   };
   L.max_tiles = max_tiles_for(np, s.E, kSkinnyBM);
+  L.max_tiles_big = max_tiles_for(np, s.E, kTilesBM);
   L.ctrl = take(sizeof(Ctrl));
   L.ids = take(np * 4);
   L.wts = take(np * 4);
@@ -58,6 +64,7 @@ Layout layout_for(const moe_shape& s) {
   L.sorted = take(np * 4);
   L.inv = take(np * 4);
   L.tiles = take((size_t)(L.max_tiles + 1) * sizeof(Tile));
+  L.tiles_big = take((size_t)(L.max_tiles_big + 1) * sizeof(Tile));
   const bool fp8 = s.wdtype == MOE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)s.T * s.H : 0);
   L.hq = take(fp8 ? (size_t)np * s.I : 0);
@@ -177,8 +184,13 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
   const Layout L = layout_for(*s);
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   Tile* tiles = at<Tile>(ws, L.tiles);
+  Tile* tiles_big = at<Tile>(ws, L.tiles_big);
+  const bool big = use_tiles(*s);
   MOE_TRY(launch_zero_words(reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
-  MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, ctrl, st));
+  if (big)
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+  else
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = x;
   if (fp8) {
     uint8_t* xq = at<uint8_t>(ws, L.xq);
@@ -187,8 +199,14 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
       return rc;
     b = xq;
   }
-  MOE_TRY(launch_w13_swiglu(s->wdtype, b, w13, w13_scale, sorted_ids, tiles, ctrl, (int)L.max_tiles,
-                            s->H, s->I, s->k, &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+  if (big)
+    MOE_TRY(launch_w13_tiles(s->wdtype, b, w13, w13_scale, sorted_ids, tiles_big,
+                             &ctrl->num_tiles_big, (int)L.max_tiles_big, s->H, s->I, s->k,
+                             &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+  else
+    MOE_TRY(launch_w13_swiglu(s->wdtype, b, w13, w13_scale, sorted_ids, tiles, ctrl,
+                              (int)L.max_tiles, s->H, s->I, s->k, &ctrl->amax_x_bits, h,
+                              &ctrl->amax_h_bits, st));
   if (fp8) MOE_TRY(launch_write_scales(ctrl, act_scales, st));
   return MOE_OK;
 }
@@ -210,7 +228,12 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   const Layout L = layout_for(*s);
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   Tile* tiles = at<Tile>(ws, L.tiles);
-  MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, ctrl, st));
+  Tile* tiles_big = at<Tile>(ws, L.tiles_big);
+  const bool big = use_tiles(*s);
+  if (big)
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+  else
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = h;
   // act_scales[3] holds amax(h) as an fp32 value; its bit pattern is what the
   // kernels read.
@@ -221,8 +244,12 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
                               amax_h, hq, st));
     b = hq;
   }
-  MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I, amax_h,
-                    y, st));
+  if (big)
+    MOE_TRY(launch_w2_tiles(s->wdtype, b, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
+                            (int)L.max_tiles_big, s->H, s->I, amax_h, y, st));
+  else
+    MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I,
+                      amax_h, y, st));
   return MOE_OK;
 }
 
@@ -273,6 +300,8 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   int32_t* inv = at<int32_t>(ws, L.inv);
   Tile* tiles = at<Tile>(ws, L.tiles);
+  Tile* tiles_big = at<Tile>(ws, L.tiles_big);
+  const bool big = use_tiles(*s);
   void* h = at<void>(ws, L.h);
   float* y = at<float>(ws, L.y);
 
@@ -282,7 +311,10 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   MOE_TRY(mark(1));
   MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
   MOE_TRY(mark(2));
-  MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, ctrl, st));
+  if (big)
+    MOE_TRY(launch_build_tiles(offsets, E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+  else
+    MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   MOE_TRY(mark(3));
   const void* bx = x;
   if (fp8) {
@@ -293,8 +325,14 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
     bx = xq;
   }
   MOE_TRY(mark(4));
-  MOE_TRY(launch_w13_swiglu(s->wdtype, bx, w13, w13_scale, sorted, tiles, ctrl, (int)L.max_tiles, H,
-                            I, k, &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+  if (big)
+    MOE_TRY(launch_w13_tiles(s->wdtype, bx, w13, w13_scale, sorted, tiles_big, &ctrl->num_tiles_big,
+                             (int)L.max_tiles_big, H, I, k, &ctrl->amax_x_bits, h,
+                             &ctrl->amax_h_bits, st));
+  else
+    MOE_TRY(launch_w13_swiglu(s->wdtype, bx, w13, w13_scale, sorted, tiles, ctrl,
+                              (int)L.max_tiles, H, I, k, &ctrl->amax_x_bits, h,
+                              &ctrl->amax_h_bits, st));
   MOE_TRY(mark(5));
   const void* bh = h;
   if (fp8) {
@@ -304,8 +342,12 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
     bh = hq;
   }
   MOE_TRY(mark(6));
-  MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,
-                    &ctrl->amax_h_bits, y, st));
+  if (big)
+    MOE_TRY(launch_w2_tiles(s->wdtype, bh, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
+                            (int)L.max_tiles_big, H, I, &ctrl->amax_h_bits, y, st));
+  else
+    MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,
+                      &ctrl->amax_h_bits, y, st));
   MOE_TRY(mark(7));
   MOE_TRY(launch_combine(s->wdtype, y, inv, wts, T, H, k, out, st));
   MOE_TRY(mark(8));

@@ -12,13 +12,12 @@
 // every weight byte is loaded once, by one lane, as part of a coalesced
 // 16-byte load, and the token operand is the small one.
 //
-// Work decomposition: a block (4 waves) owns 16 weight rows of one expert
-// for one tile of <= 16 sorted positions (one token-tile of the tile list)
-// and the whole reduction dimension K; the 4 waves split K, reduce their
-// 16x16 partial products through LDS in a fixed order, and the block
-// applies the epilogue:
-//   w13: rows 0-7 are gate rows n0..n0+7, rows 8-15 the matching up rows, so
-//        the SwiGLU h = silu(c*g) * (c*u) is formed inside the block;
+// Work decomposition: a row group is 16 weight rows of one expert for one
+// tile of <= 16 sorted positions (one entry of the tile list), over the whole
+// reduction dimension K.  A block of 4 waves takes 4/KSPLIT row groups; the
+// KSPLIT waves of a group split K and add their 16x16 partial products
+// through LDS in a fixed order.  The epilogue then forms
+//   w13: the SwiGLU h = silu(c*g) * (c*u) (gate and up rows interleaved);
 //   w2 : 16 output features of y, scaled by the FP8 dequantisation factor.
 // Scales are applied to the fp32 accumulators in the epilogue (agentic-
 // affairs.com, "Triton improves the FP8 execution path": scaling and the
@@ -96,19 +95,21 @@ struct Step<MOE_F32> {
   }
 };
 
+// Steps of loads issued ahead of their MFMAs: 128 bytes per lane in every mode
+// (deeper unrolls and non-temporal weight loads both measured slower on the
+// decode shapes).
 template <int MODE>
 constexpr int unroll_for() {
   return MODE == MOE_FP8_E4M3 ? 4 : 8;
 }
 
-// Partial product of one wave: A rows `arow` (this lane's weight row), B row
+// Partial product of one wave: A row `arow` (this lane's weight row), B row
 // `brow` (this lane's token row, or nullptr for an empty column), over the
-// wave's steps [s0, s1).
-template <int MODE>
+// wave's steps [s0, s1).  U steps of loads are issued before their MFMAs.
+template <int MODE, int U>
 __device__ __forceinline__ f32x4 wave_dot(const char* __restrict__ arow, const char* __restrict__ brow,
                                           int s0, int s1, int g) {
   typedef Step<MODE> S;
-  constexpr int U = unroll_for<MODE>();
   constexpr int STEP_BYTES = S::KS * S::ES;
   const int lane_off = g * S::LANE_K * S::ES;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -116,7 +117,9 @@ __device__ __forceinline__ f32x4 wave_dot(const char* __restrict__ arow, const c
   for (; s + U <= s1; s += U) {
     typename S::Frag a[U], b[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) a[u] = S::load(arow + (size_t)(s + u) * STEP_BYTES + lane_off);
+    for (int u = 0; u < U; u++) {
+      a[u] = S::load(arow + (size_t)(s + u) * STEP_BYTES + lane_off);
+    }
 #pragma unroll
     for (int u = 0; u < U; u++)
       b[u] = brow ? S::load(brow + (size_t)(s + u) * STEP_BYTES + lane_off) : S::zero();
@@ -136,40 +139,59 @@ __device__ __forceinline__ float act_scale_from_bits(const uint32_t* bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
-// Reduce the 4 waves' 16x16 partials; result in fin[row][col].
-__device__ __forceinline__ void block_reduce_16x16(f32x4 acc, float (*red)[16][16],
-                                                   float (*fin)[16]) {
+// Sum the KSPLIT partial 16x16 products of the waves that share a row group,
+// in a fixed order (wave 0 of the group first).  Every lane of the first wave
+// of a group gets its own 4 accumulator entries back; the other waves'
+// results are unspecified.  KSPLIT = 1 needs no exchange.
+template <int KSPLIT>
+__device__ __forceinline__ f32x4 group_reduce(f32x4 acc, float (*red)[64][4]) {
+  if (KSPLIT == 1) return acc;
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int col = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; i++) red[w][4 * g + i][col] = acc[i];
+  for (int i = 0; i < 4; i++) red[w][lane][i] = acc[i];
   __syncthreads();
-  const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
-  fin[row][c] = ((red[0][row][c] + red[1][row][c]) + red[2][row][c]) + red[3][row][c];
-  __syncthreads();
+  if (w % KSPLIT == 0) {
+#pragma unroll
+    for (int q = 1; q < KSPLIT; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[i] += red[w + q][lane][i];
+  }
+  return acc;
+}
+
+// Raise *amax_bits to v (a non-negative float) unless it is already at least
+// v: reading first keeps most waves off the single contended address; a stale
+// read only costs an atomic that changes nothing.
+__device__ __forceinline__ void amax_update(uint32_t* amax_bits, float v) {
+  const uint32_t bits = __float_as_uint(v);
+  if (bits > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, bits);
 }
 
 // ------------------------------------------------------------------- w13
-template <int MODE>
+// Block = 4 waves = 4/KSPLIT row groups, each split over K by KSPLIT waves.
+// A row group is 8 gate rows n0..n0+7 and the 8 matching up rows, interleaved
+// on the MFMA row side: MFMA row 2i is gate row n0+i, row 2i+1 up row I+n0+i.
+// The accumulator rows a lane holds (4g..4g+3) are then gate/up/gate/up of
+// features n0+2g and n0+2g+1, so the SwiGLU is formed inside the lane.
+template <int MODE, int KSPLIT, int U = unroll_for<MODE>()>
 __global__ __launch_bounds__(256) void w13_swiglu_skinny(
     const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
     const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
     const Ctrl* __restrict__ ctrl, int H, int I, int k, const uint32_t* act_amax_bits,
     void* __restrict__ h, uint32_t* amax_h_bits) {
   typedef Step<MODE> S;
-  __shared__ float red[4][16][16];
-  __shared__ float fin[16][16];
-  __shared__ float bmax[4];
-  const int n_rt = I / 8;
-  const int tile_idx = blockIdx.x / n_rt;
-  const int rt = blockIdx.x - tile_idx * n_rt;
+  constexpr int RG = 4 / KSPLIT;
+  __shared__ float red[KSPLIT > 1 ? 4 : 1][64][4];
+  const int blocks_per_tile = I / (8 * RG);
+  const int tile_idx = blockIdx.x / blocks_per_tile;
+  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
   if (tile_idx >= ctrl->num_tiles) return;
   const Tile tl = tiles[tile_idx];
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = rt * 8;
-  // this lane's weight row: gate rows n0..n0+7, then up rows I+n0..I+n0+7
-  const int wrow = (r < 8) ? (n0 + r) : (I + n0 + r - 8);
+  const int n0 = (rb * RG + w / KSPLIT) * 8;
+  const int kp = w % KSPLIT;
+  const int wrow = (r & 1) ? (I + n0 + (r >> 1)) : (n0 + (r >> 1));
   const char* arow = w13 + ((size_t)tl.e * 2 * I + wrow) * (size_t)H * S::ES;
   const char* brow = nullptr;
   if (r < tl.mt) {
@@ -177,45 +199,46 @@ __global__ __launch_bounds__(256) void w13_swiglu_skinny(
     brow = b + (size_t)tok * H * S::ES;
   }
   const int n_steps = H / S::KS;
-  const int s0 = (w * n_steps) / 4, s1 = ((w + 1) * n_steps) / 4;
-  f32x4 acc = wave_dot<MODE>(arow, brow, s0, s1, g);
-  block_reduce_16x16(acc, red, fin);
+  const int s0 = (kp * n_steps) / KSPLIT, s1 = ((kp + 1) * n_steps) / KSPLIT;
+  f32x4 acc = wave_dot<MODE, U>(arow, brow, s0, s1, g);
+  acc = group_reduce<KSPLIT>(acc, red);
+  if (kp != 0) return;
 
   float c = 1.0f;
   if (MODE == MOE_FP8_E4M3) c = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
   float hmax = 0.f;
-  if (threadIdx.x < 128) {
-    const int j = threadIdx.x >> 3, rr = threadIdx.x & 7;
-    if (j < tl.mt) {
-      float gv = fin[rr][j], uv = fin[rr + 8][j];
+  if (r < tl.mt) {
+    float hv[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      float gv = acc[2 * q], uv = acc[2 * q + 1];
       if (MODE == MOE_FP8_E4M3) {
         gv *= c;
         uv *= c;
       }
-      float hv = gv / (1.0f + expf(-gv)) * uv;
-      size_t o = (size_t)(tl.p0 + j) * I + n0 + rr;
-      if (MODE == MOE_F32) {
-        reinterpret_cast<float*>(h)[o] = hv;
-      } else {
-        uint16_t hb = f32_to_bf16(hv);
-        reinterpret_cast<uint16_t*>(h)[o] = hb;
-        hmax = fabsf(bf16_to_f32(hb));
-      }
+      hv[q] = gv / (1.0f + expf(-gv)) * uv;
+    }
+    size_t o = (size_t)(tl.p0 + r) * I + n0 + 2 * g;
+    if (MODE == MOE_F32) {
+      *reinterpret_cast<float2*>(reinterpret_cast<float*>(h) + o) = make_float2(hv[0], hv[1]);
+    } else {
+      uint16_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(h) + o) =
+          (uint32_t)h0 | ((uint32_t)h1 << 16);
+      hmax = fmaxf(fabsf(bf16_to_f32(h0)), fabsf(bf16_to_f32(h1)));
     }
   }
   if (MODE == MOE_FP8_E4M3) {
     hmax = wave_max(hmax);
-    if (lane == 0) bmax[w] = hmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float m = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
-      atomicMax(amax_h_bits, __float_as_uint(m));
-    }
+    if (lane == 0) amax_update(amax_h_bits, hmax);
   }
 }
 
 // -------------------------------------------------------------------- w2
-template <int MODE>
+// Block = 4/KSPLIT row groups of 16 output features m0..m0+15, each split over
+// K by KSPLIT waves.  A lane's accumulator rows 4g..4g+3 are 4 consecutive
+// features of its token column: one 16-byte store of y.
+template <int MODE, int KSPLIT, int U = unroll_for<MODE>()>
 __global__ __launch_bounds__(256) void w2_skinny(const char* __restrict__ b,
                                                  const char* __restrict__ w2,
                                                  const float* __restrict__ w2_scale,
@@ -224,78 +247,93 @@ __global__ __launch_bounds__(256) void w2_skinny(const char* __restrict__ b,
                                                  const uint32_t* act_amax_bits,
                                                  float* __restrict__ y) {
   typedef Step<MODE> S;
-  __shared__ float red[4][16][16];
-  __shared__ float fin[16][16];
-  const int n_rt = H / 16;
-  const int tile_idx = blockIdx.x / n_rt;
-  const int rt = blockIdx.x - tile_idx * n_rt;
+  constexpr int RG = 4 / KSPLIT;
+  __shared__ float red[KSPLIT > 1 ? 4 : 1][64][4];
+  const int blocks_per_tile = H / (16 * RG);
+  const int tile_idx = blockIdx.x / blocks_per_tile;
+  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
   if (tile_idx >= ctrl->num_tiles) return;
   const Tile tl = tiles[tile_idx];
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int m0 = rt * 16;
+  const int m0 = (rb * RG + w / KSPLIT) * 16;
+  const int kp = w % KSPLIT;
   const char* arow = w2 + ((size_t)tl.e * H + m0 + r) * (size_t)I * S::ES;
   const char* brow = (r < tl.mt) ? b + (size_t)(tl.p0 + r) * I * S::ES : nullptr;
   const int n_steps = I / S::KS;
-  const int s0 = (w * n_steps) / 4, s1 = ((w + 1) * n_steps) / 4;
-  f32x4 acc = wave_dot<MODE>(arow, brow, s0, s1, g);
-  block_reduce_16x16(acc, red, fin);
-  float c = 1.0f;
-  if (MODE == MOE_FP8_E4M3) c = act_scale_from_bits(act_amax_bits) * w2_scale[tl.e];
-  const int j = threadIdx.x >> 4, mm = threadIdx.x & 15;
-  if (j < tl.mt) {
-    float v = fin[mm][j];
-    if (MODE == MOE_FP8_E4M3) v *= c;
-    y[(size_t)(tl.p0 + j) * H + m0 + mm] = v;
-  }
+  const int s0 = (kp * n_steps) / KSPLIT, s1 = ((kp + 1) * n_steps) / KSPLIT;
+  f32x4 acc = wave_dot<MODE, U>(arow, brow, s0, s1, g);
+  acc = group_reduce<KSPLIT>(acc, red);
+  if (kp != 0 || r >= tl.mt) return;
+  if (MODE == MOE_FP8_E4M3) acc *= act_scale_from_bits(act_amax_bits) * w2_scale[tl.e];
+  *reinterpret_cast<f32x4*>(y + (size_t)(tl.p0 + r) * H + m0 + 4 * g) = acc;
+}
+
+// Waves per row group that split the reduction dimension.  All four waves of
+// a block work on the same 16 rows: the block's concurrent loads then fall in
+// the same DRAM pages, which measured faster than giving each wave its own
+// rows for every decode shape.
+template <int MODE>
+constexpr int ksplit_w13() {
+  return 4;
+}
+template <int MODE>
+constexpr int ksplit_w2() {
+  return 4;
+}
+
+template <int MODE>
+static void launch_w13_mode(long max_tiles, const char* b, const char* w13, const float* w13_scale,
+                            const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl, int H,
+                            int I, int k, const uint32_t* act_amax_bits, void* h,
+                            uint32_t* amax_h_bits, hipStream_t st) {
+  constexpr int KS = ksplit_w13<MODE>();
+  const long blocks = max_tiles * (I / (8 * (4 / KS)));
+  w13_swiglu_skinny<MODE, KS><<<blocks, 256, 0, st>>>(b, w13, w13_scale, sorted_ids, tiles, ctrl, H,
+                                                      I, k, act_amax_bits, h, amax_h_bits);
+}
+
+template <int MODE>
+static void launch_w2_mode(long max_tiles, const char* b, const char* w2, const float* w2_scale,
+                           const Tile* tiles, const Ctrl* ctrl, int H, int I,
+                           const uint32_t* act_amax_bits, float* y, hipStream_t st) {
+  constexpr int KS = ksplit_w2<MODE>();
+  const long blocks = max_tiles * (H / (16 * (4 / KS)));
+  w2_skinny<MODE, KS><<<blocks, 256, 0, st>>>(b, w2, w2_scale, tiles, ctrl, H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const float* w13_scale,
                              const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl,
                              int max_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
                              void* h, uint32_t* amax_h_bits, hipStream_t st) {
-  long blocks = (long)max_tiles * (I / 8);
-  if (blocks <= 0) return hipSuccess;
+  if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w13);
-  switch (mode) {
-    case MOE_F32:
-      w13_swiglu_skinny<MOE_F32><<<blocks, 256, 0, st>>>(bb, ww, w13_scale, sorted_ids, tiles, ctrl,
-                                                         H, I, k, act_amax_bits, h, amax_h_bits);
-      break;
-    case MOE_BF16:
-      w13_swiglu_skinny<MOE_BF16><<<blocks, 256, 0, st>>>(bb, ww, w13_scale, sorted_ids, tiles,
-                                                          ctrl, H, I, k, act_amax_bits, h,
-                                                          amax_h_bits);
-      break;
-    default:
-      w13_swiglu_skinny<MOE_FP8_E4M3><<<blocks, 256, 0, st>>>(bb, ww, w13_scale, sorted_ids, tiles,
-                                                              ctrl, H, I, k, act_amax_bits, h,
-                                                              amax_h_bits);
-  }
+  if (mode == MOE_F32)
+    launch_w13_mode<MOE_F32>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
+                             act_amax_bits, h, amax_h_bits, st);
+  else if (mode == MOE_BF16)
+    launch_w13_mode<MOE_BF16>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
+                              act_amax_bits, h, amax_h_bits, st);
+  else
+    launch_w13_mode<MOE_FP8_E4M3>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
+                                  act_amax_bits, h, amax_h_bits, st);
   return hipGetLastError();
 }
 
 hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
                      const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
                      const uint32_t* act_amax_bits, float* y, hipStream_t st) {
-  long blocks = (long)max_tiles * (H / 16);
-  if (blocks <= 0) return hipSuccess;
+  if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w2);
-  switch (mode) {
-    case MOE_F32:
-      w2_skinny<MOE_F32><<<blocks, 256, 0, st>>>(bb, ww, w2_scale, tiles, ctrl, H, I,
-                                                 act_amax_bits, y);
-      break;
-    case MOE_BF16:
-      w2_skinny<MOE_BF16><<<blocks, 256, 0, st>>>(bb, ww, w2_scale, tiles, ctrl, H, I,
-                                                  act_amax_bits, y);
-      break;
-    default:
-      w2_skinny<MOE_FP8_E4M3><<<blocks, 256, 0, st>>>(bb, ww, w2_scale, tiles, ctrl, H, I,
-                                                      act_amax_bits, y);
-  }
+  if (mode == MOE_F32)
+    launch_w2_mode<MOE_F32>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, st);
+  else if (mode == MOE_BF16)
+    launch_w2_mode<MOE_BF16>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, st);
+  else
+    launch_w2_mode<MOE_FP8_E4M3>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y,
+                                 st);
   return hipGetLastError();
 }
 

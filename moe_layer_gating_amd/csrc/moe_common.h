@@ -10,6 +10,8 @@
 namespace moe {
 
 constexpr int kWave = 64;
+constexpr int kSkinnyBM = 16;  // sorted positions per tile of the few-token GEMMs
+constexpr int kTilesBM = 128;  // sorted positions per tile of the many-token GEMMs
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -25,10 +27,11 @@ struct Tile {
 // Control words at the start of the workspace (zeroed at the start of a call
 // by the first kernel that runs).
 struct Ctrl {
-  uint32_t amax_x_bits;  // max |x| as fp32 bits (non-negative floats order as uints)
-  uint32_t amax_h_bits;  // max |h| as fp32 bits
-  int32_t num_tiles;     // tiles written by the tile builder
-  int32_t pad[61];
+  uint32_t amax_x_bits;    // max |x| as fp32 bits (non-negative floats order as uints)
+  uint32_t amax_h_bits;    // max |h| as fp32 bits
+  int32_t num_tiles;       // tiles of <= kSkinnyBM positions written by the tile builder
+  int32_t num_tiles_big;   // tiles of <= kTilesBM positions
+  int32_t pad[60];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl block is one 256-byte slot");
 
@@ -82,8 +85,8 @@ hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int reno
 hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
                              hipStream_t st);
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles, Ctrl* ctrl,
-                              hipStream_t st);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
+                              int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
 hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hipStream_t st);
 hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_bits, uint8_t* dst,
@@ -99,6 +102,16 @@ hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const flo
 hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
                      const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
                      const uint32_t* act_amax_bits, float* y, hipStream_t st);
+// Many-token variants (bf16 and FP8 only); the tile count is read from
+// *num_tiles on the device.
+hipError_t launch_w13_tiles(int mode, const void* b, const void* w13, const float* w13_scale,
+                            const int32_t* sorted_ids, const Tile* tiles,
+                            const int32_t* num_tiles, int max_tiles, int H, int I, int k,
+                            const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
+                            hipStream_t st);
+hipError_t launch_w2_tiles(int mode, const void* b, const void* w2, const float* w2_scale,
+                           const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
+                           int I, const uint32_t* act_amax_bits, float* y, hipStream_t st);
 hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,
                           int H, int k, void* out, hipStream_t st);
 

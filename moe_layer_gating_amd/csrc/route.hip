@@ -214,10 +214,10 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* c
 // -------------------------------------------------------------- tile list
 // One block of 256 threads.  Expert e with c = offsets[e+1]-offsets[e] pairs
 // contributes ceil(c / bm) tiles of at most bm consecutive sorted positions;
-// tiles are listed expert by expert.  The tile count goes to ctrl->num_tiles.
+// tiles are listed expert by expert.  The tile count goes to *num_tiles.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int bm, Tile* __restrict__ tiles,
-                                                          Ctrl* ctrl) {
+                                                          int32_t* num_tiles) {
   __shared__ int tmp[4];
   int local[4], s = 0;
 #pragma unroll
@@ -245,12 +245,12 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
     }
     pre += local[q];
   }
-  if (threadIdx.x == 0) ctrl->num_tiles = total;
+  if (threadIdx.x == 0) *num_tiles = total;
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles, Ctrl* ctrl,
-                              hipStream_t st) {
-  build_tiles_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tiles, ctrl);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
+                              int32_t* num_tiles, hipStream_t st) {
+  build_tiles_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tiles, num_tiles);
   return hipGetLastError();
 }
 

@@ -38,6 +38,12 @@ CASES = [
     ("fp8_empty", 40, 384, 20, 4, 256, FP8, "empty"),
     ("fp8_t1", 1, 512, 64, 8, 256, FP8, "uniform"),
     ("fp8_k_equals_E", 6, 256, 4, 4, 128, FP8, "uniform"),
+    # many pairs per expert: the 128-position tiled GEMMs (several tiles per
+    # expert, ragged last tiles, 8+ weight-row blocks, empty and skewed experts)
+    ("fp8_tiles_ragged", 600, 512, 8, 2, 512, FP8, "uniform"),
+    ("bf16_tiles_zipf", 256, 384, 16, 4, 384, BF16, "zipf"),
+    ("fp8_tiles_empty", 256, 256, 16, 4, 640, FP8, "empty"),
+    ("bf16_tiles_one_expert", 200, 256, 1, 1, 512, BF16, "uniform"),
 ]
 IDS = [c[0] for c in CASES]
 
