@@ -40,10 +40,13 @@ struct Layout {
 
 // Shape class: the many-token tiled GEMMs once experts receive 16 or more
 // pairs on average (bf16 and FP8); the few-token swap-AB GEMMs otherwise.
+// The tiled GEMMs use 64-position tiles while the mean is below 64 pairs
+// per expert (less padding), 128-position tiles above (more weight reuse).
 // Decided from the shape alone, so no per-call specialisation arises.
 inline bool use_tiles(const moe_shape& s) {
   return s.wdtype != MOE_F32 && (long)s.T * s.k >= 16L * s.E;
 }
+inline int tiles_bm(const moe_shape& s) { return (long)s.T * s.k < 64L * s.E ? 64 : 128; }
 
 Layout layout_for(const moe_shape& s) {
   Layout L;
@@ -55,7 +58,7 @@ Layout layout_for(const moe_shape& s) {
     return at;
   };
   L.max_tiles = max_tiles_for(np, s.E, kSkinnyBM);
-  L.max_tiles_big = max_tiles_for(np, s.E, kTilesBM);
+  L.max_tiles_big = max_tiles_for(np, s.E, tiles_bm(s));
   L.ctrl = take(sizeof(Ctrl));
   L.ids = take(np * 4);
   L.wts = take(np * 4);
@@ -188,7 +191,7 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
   const bool big = use_tiles(*s);
   MOE_TRY(launch_zero_words(reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
   if (big)
-    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
   else
     MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = x;
@@ -200,7 +203,7 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
     b = xq;
   }
   if (big)
-    MOE_TRY(launch_w13_tiles(s->wdtype, b, w13, w13_scale, sorted_ids, tiles_big,
+    MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), b, w13, w13_scale, sorted_ids, tiles_big,
                              &ctrl->num_tiles_big, (int)L.max_tiles_big, s->H, s->I, s->k,
                              &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
   else
@@ -231,7 +234,7 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   Tile* tiles_big = at<Tile>(ws, L.tiles_big);
   const bool big = use_tiles(*s);
   if (big)
-    MOE_TRY(launch_build_tiles(expert_offsets, s->E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
   else
     MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = h;
@@ -245,7 +248,7 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
     b = hq;
   }
   if (big)
-    MOE_TRY(launch_w2_tiles(s->wdtype, b, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
+    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), b, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
                             (int)L.max_tiles_big, s->H, s->I, amax_h, y, st));
   else
     MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I,
@@ -312,7 +315,7 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
   MOE_TRY(mark(2));
   if (big)
-    MOE_TRY(launch_build_tiles(offsets, E, kTilesBM, tiles_big, &ctrl->num_tiles_big, st));
+    MOE_TRY(launch_build_tiles(offsets, E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
   else
     MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   MOE_TRY(mark(3));
@@ -326,7 +329,7 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   }
   MOE_TRY(mark(4));
   if (big)
-    MOE_TRY(launch_w13_tiles(s->wdtype, bx, w13, w13_scale, sorted, tiles_big, &ctrl->num_tiles_big,
+    MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), bx, w13, w13_scale, sorted, tiles_big, &ctrl->num_tiles_big,
                              (int)L.max_tiles_big, H, I, k, &ctrl->amax_x_bits, h,
                              &ctrl->amax_h_bits, st));
   else
@@ -343,7 +346,7 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   }
   MOE_TRY(mark(6));
   if (big)
-    MOE_TRY(launch_w2_tiles(s->wdtype, bh, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
+    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), bh, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
                             (int)L.max_tiles_big, H, I, &ctrl->amax_h_bits, y, st));
   else
     MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,

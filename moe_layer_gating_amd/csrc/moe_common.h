@@ -11,7 +11,7 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kSkinnyBM = 16;  // sorted positions per tile of the few-token GEMMs
-constexpr int kTilesBM = 128;  // sorted positions per tile of the many-token GEMMs
+constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -30,7 +30,7 @@ struct Ctrl {
   uint32_t amax_x_bits;    // max |x| as fp32 bits (non-negative floats order as uints)
   uint32_t amax_h_bits;    // max |h| as fp32 bits
   int32_t num_tiles;       // tiles of <= kSkinnyBM positions written by the tile builder
-  int32_t num_tiles_big;   // tiles of <= kTilesBM positions
+  int32_t num_tiles_big;   // tiles of the many-token GEMMs
   int32_t pad[60];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl block is one 256-byte slot");
@@ -102,14 +102,14 @@ hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const flo
 hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
                      const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
                      const uint32_t* act_amax_bits, float* y, hipStream_t st);
-// Many-token variants (bf16 and FP8 only); the tile count is read from
-// *num_tiles on the device.
-hipError_t launch_w13_tiles(int mode, const void* b, const void* w13, const float* w13_scale,
-                            const int32_t* sorted_ids, const Tile* tiles,
+// Many-token variants (bf16 and FP8 only; tiles of bm = 64 or 128 sorted
+// positions); the tile count is read from *num_tiles on the device.
+hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
+                            const float* w13_scale, const int32_t* sorted_ids, const Tile* tiles,
                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                             const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
                             hipStream_t st);
-hipError_t launch_w2_tiles(int mode, const void* b, const void* w2, const float* w2_scale,
+hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, const float* w2_scale,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
                            int I, const uint32_t* act_amax_bits, float* y, hipStream_t st);
 hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,

@@ -67,10 +67,10 @@ def _load():
         lib.oracle_act_quant.argtypes = [P, i32, i64, P, P]
         lib.oracle_w13_swiglu.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P]
         lib.oracle_w2.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
-        lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         lib.oracle_combine_f32.argtypes = [i32, i32, i32, i32, P, P, P, P]
         lib.oracle_forward.restype = ctypes.c_int
-        lib.oracle_forward.argtypes = [i32] * 7 + [P] * 15
+        lib.oracle_forward.argtypes = [i32] * 7 + [P] * 16
         _lib = lib
     return _lib
 
@@ -210,12 +210,13 @@ def combine(mode, y, inv_perm, topk_weights):
         _load().oracle_combine_f32(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out))
     else:
         yy = _c(y, np.float64)
-        _load().oracle_combine(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out))
+        _load().oracle_combine(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out), None)
     return out
 
 
 def forward(mode, x, logits, w13, w13_scale, w2_, w2_scale, k, renormalize=True):
-    """The whole layer.  Returns a dict with out and every intermediate."""
+    """The whole layer.  Returns a dict with out and every intermediate;
+    ``out_exact`` holds out before its rounding to the output type."""
     x = _c(x, act_dtype(mode))
     logits = _c(logits, np.float32)
     w13 = _c(w13, w_dtype(mode))
@@ -235,11 +236,13 @@ def forward(mode, x, logits, w13, w13_scale, w2_, w2_scale, k, renormalize=True)
         inv_perm=np.empty(T * k, np.int32),
         h=np.empty((T * k, I), act_dtype(mode)),
         scales=np.empty(2, np.float32),
+        out_exact=np.empty((T, H), np.float64),
     )
     rc = _load().oracle_forward(mode, T, H, E, k, I, int(bool(renormalize)), _p(x), _p(logits),
                                 _p(w13), _p(s13), _p(w2_), _p(s2), _p(r["out"]), _p(r["topk_ids"]),
                                 _p(r["topk_weights"]), _p(r["counts"]), _p(r["offsets"]),
-                                _p(r["sorted_ids"]), _p(r["inv_perm"]), _p(r["h"]), _p(r["scales"]))
+                                _p(r["sorted_ids"]), _p(r["inv_perm"]), _p(r["h"]), _p(r["scales"]),
+                                _p(r["out_exact"]))
     if rc != 0:
         raise MemoryError("oracle_forward: allocation failed")
     return r

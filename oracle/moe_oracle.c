@@ -391,10 +391,11 @@ void oracle_w2(int wdtype, int T, int H, int E, int k, int I, const void* h, con
 /* agentic-affairs.com FP8 section).                                          */
 /*   out[t,m] = sum_{j<k} w[t,j] * y[inv_perm[t*k+j], m], in slot order,      */
 /* rounded once to the output type.                                           */
-/* y is indexed by sorted position and given in double.                      */
+/* y is indexed by sorted position and given in double.  out_exact (may be   */
+/* NULL) receives the same sums before that final rounding.                  */
 /* ------------------------------------------------------------------------ */
 void oracle_combine(int wdtype, int T, int H, int k, const double* y, const int32_t* inv_perm,
-                    const float* topk_weights, void* out) {
+                    const float* topk_weights, void* out, double* out_exact) {
 #pragma omp parallel for collapse(2)
   for (int t = 0; t < T; t++) {
     for (int m = 0; m < H; m++) {
@@ -404,6 +405,7 @@ void oracle_combine(int wdtype, int T, int H, int k, const double* y, const int3
         acc += (double)topk_weights[(size_t)t * k + j] * y[(size_t)p * H + m];
       }
       astore(out, wdtype, (size_t)t * H + m, acc);
+      if (out_exact) out_exact[(size_t)t * H + m] = acc;
     }
   }
 }
@@ -429,14 +431,16 @@ void oracle_combine_f32(int wdtype, int T, int H, int k, const float* y, const i
 /* down projection, aggregation.  Because the FP8 scale of h is a maximum    */
 /* over every routed pair, all of h is finished before any down projection. */
 /* Optional outputs (may be NULL): topk ids/weights, counts, offsets,         */
-/* sorted ids, inverse permutation, h (sorted order), scales[2] = s_x, s_h.  */
+/* sorted ids, inverse permutation, h (sorted order), scales[2] = s_x, s_h,  */
+/* out_exact = out before its rounding to the output type (double).          */
 /* Returns 0, or -1 if an allocation fails.                                   */
 /* ------------------------------------------------------------------------ */
 int oracle_forward(int wdtype, int T, int H, int E, int k, int I, int renormalize,
                    const void* x, const float* logits, const void* w13, const float* w13_scale,
                    const void* w2, const float* w2_scale, void* out, int32_t* ids_out,
                    float* w_out, int32_t* counts_out, int32_t* offsets_out,
-                   int32_t* sorted_out, int32_t* inv_out, void* h_out, float* scales_out) {
+                   int32_t* sorted_out, int32_t* inv_out, void* h_out, float* scales_out,
+                   double* out_exact) {
   long n_pairs = (long)T * k;
   size_t abytes = (wdtype == MOE_F32) ? 4 : 2;
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_pairs + 1));
@@ -455,7 +459,7 @@ int oracle_forward(int wdtype, int T, int H, int E, int k, int I, int renormaliz
   oracle_w13_swiglu(wdtype, T, H, E, k, I, x, w13, w13_scale, sorted_ids, offsets, NULL, 0, h,
                     &s_x);
   oracle_w2(wdtype, T, H, E, k, I, h, w2, w2_scale, offsets, NULL, 0, y, &s_h);
-  oracle_combine(wdtype, T, H, k, y, inv, w, out);
+  oracle_combine(wdtype, T, H, k, y, inv, w, out, out_exact);
 
   if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)n_pairs);
   if (w_out) memcpy(w_out, w, sizeof(float) * (size_t)n_pairs);

@@ -64,6 +64,22 @@ def rel_inf(gpu, ref):
     return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0)) if ref.size else 0.0
 
 
+def bf16_step_ratio(gpu, ref):
+    """Largest |gpu - ref| / (ulp(ref) + 2^-9 max|ref|) over the elements, ulp
+    being the bf16 spacing at |ref| (2^(floor(log2|ref|) - 7)).  At most 1
+    means: every element is within one bf16 step of the reference, or within
+    half a bf16 step at the tensor's largest magnitude; the second term covers
+    elements near zero that come from cancelling sums, whose absolute
+    accumulation error is set by the size of the summands, not of the result."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not gpu.size:
+        return 0.0
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    bound = ulp + 2.0 ** -9 * np.max(np.abs(ref))
+    return float(np.max(np.abs(gpu - ref) / bound))
+
+
 # tolerance on the layer output, max |gpu - ref| / max |ref|
 OUT_TOL = {F32: 1e-5, BF16: 5e-3, FP8: 2e-2}
 

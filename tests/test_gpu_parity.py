@@ -5,12 +5,16 @@ tiles, ragged tails (experts with token counts that are not multiples of the
 16-wide tile), skewed and empty experts, T = 1, k = 1, E = 1 and k = E.
 
 Bars: routing (ids, counts, offsets, sorted ids, inverse permutation) and
-the FP8 activation scales are bit-exact; values are within the per-mode
-tolerance on max|gpu - ref| / max|ref| (fp32 1e-5, bf16 5e-3, FP8 2e-2).
-Stage bars are tighter: h within one bf16 step of the oracle; y (fp32) within
-1e-5, except FP8 where the gfx950 FP8 MFMA's own accumulation error (median
-~3e-5 relative per dot product, measured) sets the bar at 2e-4 and the share
-of bit-identical bf16 h values at 95%.
+the FP8 activation scales are bit-exact; the layer output is within the
+per-mode tolerance on max|gpu - ref| / max|ref| (fp32 1e-5, bf16 5e-3, FP8
+2e-2), ref being the oracle's output before its final rounding to the
+output type (both sides rounding to bf16 could otherwise differ by one
+output ulp, up to 2^-7 of max|ref|, for results that are both correct).
+Stage bars are tighter: h within one bf16 step of the oracle (see
+gpu_helpers.bf16_step_ratio); y (fp32) within 1e-5, except FP8 where the
+gfx950 FP8 MFMA's own accumulation error (median ~3e-5 relative per dot
+product, measured) sets the bar at 2e-4 and the share of bit-identical bf16 h
+values at 95%.
 Each stage is fed the oracle's upstream outputs so a failure names its stage.
 """
 import numpy as np
@@ -20,8 +24,8 @@ import torch
 import moe_layer_gating_amd as moe
 import moe_workloads as wl
 import oracle
-from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, f32_tensor,
-                         int_tensor, rel_inf, say, upload)
+from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, bf16_step_ratio,
+                         f32_tensor, int_tensor, rel_inf, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +48,9 @@ CASES = [
     ("bf16_tiles_zipf", 256, 384, 16, 4, 384, BF16, "zipf"),
     ("fp8_tiles_empty", 256, 256, 16, 4, 640, FP8, "empty"),
     ("bf16_tiles_one_expert", 200, 256, 1, 1, 512, BF16, "uniform"),
+    # 16 <= mean pairs per expert < 64: 64-position tiles, some experts spill
+    # into a second tile
+    ("fp8_tiles64_ragged", 250, 384, 8, 2, 384, FP8, "uniform"),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -105,7 +112,9 @@ def test_w13_swiglu(c):
     if mode == F32:
         assert rel_inf(hv, rv) <= 1e-5
     else:
-        assert rel_inf(hv, rv) <= 4e-3
+        # every element within one bf16 step of the oracle's (see
+        # bf16_step_ratio), almost all equal
+        assert bf16_step_ratio(hv, rv) <= 1.0
         assert np.mean(hg == ref["h"]) > (0.95 if mode == FP8 else 0.99)
     if mode == FP8:
         s = sc.cpu().numpy()
@@ -170,7 +179,8 @@ def test_fused_forward(c):
     assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
     og = oracle.to_f64(act_to_numpy(out, mode), mode)
     assert not np.isnan(og).any()  # every row written
-    err = rel_inf(og, oracle.to_f64(ref["out"], mode))
+    # reference: the oracle's output before its rounding to the output type
+    err = rel_inf(og, ref["out_exact"])
     say("  rel err", err)
     assert err <= OUT_TOL[mode]
     # a second call gives bit-identical results

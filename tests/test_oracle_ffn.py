@@ -172,3 +172,17 @@ def test_steps_compose_to_forward(mode):
     assert np.array_equal(hs, h[pos])
     ys, _ = oracle.w2(mode, h, L["w2"], L["w2_scale"], offsets, k, positions=pos)
     assert np.array_equal(ys, y[pos])
+
+
+@pytest.mark.parametrize("mode", [F32, BF16, FP8])
+def test_out_is_the_rounding_of_out_exact(mode):
+    """The stored output is the output type's rounding of out_exact."""
+    L = _layer(9, 64, 8, 2, 48, mode, seed=4 + mode)
+    s = L["spec"]
+    r = oracle.forward(mode, L["x"], L["logits"], L["w13"], L["w13_scale"], L["w2"], L["w2_scale"],
+                       s.k)
+    if mode == F32:
+        assert np.array_equal(r["out"], r["out_exact"].astype(np.float32))
+    else:
+        assert np.array_equal(r["out"].ravel(), bf.f64_to_bf16_values(r["out_exact"]).astype(
+            np.float32).view(np.uint32).ravel().__rshift__(16).astype(np.uint16))
