@@ -2,24 +2,31 @@
 """Benchmark of the fused MoE layer on one MI355X.
 
 One step = one call of moe_fused_forward over one batch: gating, grouping,
-(FP8: activation quantisation), gate/up GEMM + SwiGLU, down GEMM and the
-weighted combine, with every input already resident in HBM.
+(FP8: activation quantisation), gate/up GEMM + SwiGLU, (FP8: h quantisation),
+down GEMM and the weighted combine, with every input already resident in HBM.
 
 Default workload: the bf16 decode layer (8 tokens, hidden 4096, 8 experts,
 top-2, SwiGLU intermediate 14336), the shape the headline metric is quoted
-on.  Inputs are seeded synthetic tensors (moe_workloads).
+on.  Other layers: --workload decode_fp8_t1 | decode_fp8_t4 | decode_fp8_t16 |
+mixed_fp8 | prefill_fp8 | tiny_f32.  Inputs are seeded synthetic tensors
+(moe_workloads).
 
 Prints ONE JSON line with tokens/s as `value`, plus:
-  roofline     -- the dominant kernel (the gate/up GEMM): algorithmic bytes
-                  per launch / its average duration, timed with HIP events
-                  recorded around it inside the fused call, against 8 TB/s;
+  roofline     -- the dominant kernel (the gate/up GEMM): its algorithmic
+                  bytes per launch / its average duration, timed with HIP
+                  events recorded on the launch stream around that kernel in
+                  every timed step, against 8 TB/s; `traffic` = its HBM bytes
+                  per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+                  (profiles/traffic.json), null when the kernel sources have
+                  changed since those counters were taken;
   cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
-                  the same workload (whole layers, repeated ~10 s).
+                  the same workload (whole layers, about 10 s).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -31,7 +38,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0}  # dense fp32 / bf16 / fp8
 METRIC = "fused-MoE layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
-DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8"}
+DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8e4m3"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "moe_layer_gating_amd", "csrc")
 
 
 def hip():
@@ -44,6 +53,35 @@ def hip():
     return h
 
 
+def kernel_sources(big):
+    """Source files that define the dominant kernel of a shape class."""
+    names = ["gemm_tiles.hip" if big else "gemm_skinny.hip", "moe_common.h"]
+    return [os.path.join(CSRC, n) for n in names]
+
+
+def sources_sha256(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload, kernel, big):
+    """HBM bytes per launch of the dominant kernel from the stored counter
+    runs, or None if there are none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel") != kernel:
+        return None
+    if rec.get("sources_sha256") != sources_sha256(kernel_sources(big)):
+        return None
+    return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024
+
+
 def algorithmic(spec, counts):
     """Bytes / flops the method must move / compute (padding excluded)."""
     T, H, E, k, I, mode = spec.T, spec.H, spec.E, spec.k, spec.I, spec.mode
@@ -53,9 +91,12 @@ def algorithmic(spec, counts):
     scale_b = 8 * active if mode == 2 else 0
     layer_bytes = active * 3 * H * I * bw + scale_b + T * H * bx + 4 * T * E + T * H * bx
     flops = 6.0 * T * k * H * I
+    # gate/up kernel: the active experts' w13 rows (+ FP8 scales), the token
+    # rows it reads (e4m3 codes in FP8 mode) and the h it writes
     w13_bytes = active * 2 * I * H * bw + (4 * active if mode == 2 else 0) + T * H * (
         1 if mode == 2 else bx) + T * k * I * bx
-    return active, layer_bytes, flops, w13_bytes
+    w13_flops = 4.0 * T * k * H * I
+    return active, layer_bytes, flops, w13_bytes, w13_flops
 
 
 def cpu_baseline(L, budget_s=10.0):
@@ -141,9 +182,28 @@ def main():
     ws = moe.workspace(shape)
     out = torch.empty((spec.T, spec.H), dtype=moe.act_dtype(mode), device="cuda")
     ids = torch.empty((spec.T, spec.k), dtype=torch.int32, device="cuda")
+    big = mode != 0 and spec.T * spec.k >= 16 * spec.E  # the tiled shape class
+    kernel = "w13_swiglu_tiles" if big else "w13_swiglu_skinny"
 
-    def step():
-        moe.moe_fused_forward(x, logits, w13, s13, w2, s2, spec.k, out=out, ws=ws, topk_ids=ids)
+    H_ = hip()
+
+    def new_event():
+        e = ctypes.c_void_p()
+        assert H_.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(a, b):
+        f = ctypes.c_float()
+        assert H_.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return f.value
+
+    def step(events=None):
+        if events is None:
+            moe.moe_fused_forward(x, logits, w13, s13, w2, s2, spec.k, out=out, ws=ws,
+                                  topk_ids=ids)
+        else:
+            moe.moe_fused_forward_events(x, logits, w13, s13, w2, s2, spec.k, events, out=out,
+                                         ws=ws, topk_ids=ids)
 
     print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -151,39 +211,34 @@ def main():
     torch.cuda.synchronize()
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=spec.E)
 
+    # timed region: every step records an event pair around the gate/up GEMM
+    # (stage boundaries 4 and 5) on the stream the kernels run on
+    pairs = [(new_event(), new_event()) for _ in range(args.steps)]
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for a, b in pairs:
+        step([None, None, None, None, a, b, None, None, None])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
+    w13_ms = float(np.mean([elapsed_ms(a, b) for a, b in pairs]))
 
-    # dominant kernel: HIP events recorded around each stage inside the fused call
-    H_ = hip()
-    evs = []
-    for _ in range(moe.NUM_STAGE_EVENTS):
-        e = ctypes.c_void_p()
-        assert H_.hipEventCreate(ctypes.byref(e)) == 0
-        evs.append(e.value)
-    reps = max(args.steps, 10)
+    # per-stage breakdown (outside the timed region; every boundary recorded)
+    evs = [new_event() for _ in range(moe.NUM_STAGE_EVENTS)]
+    reps = min(args.steps, 20)
     stage_ms = np.zeros(moe.NUM_STAGE_EVENTS - 1)
     for _ in range(reps):
-        moe.moe_fused_forward_events(x, logits, w13, s13, w2, s2, spec.k, evs, out=out, ws=ws,
-                                     topk_ids=ids)
+        step(evs)
         H_.hipEventSynchronize(ctypes.c_void_p(evs[-1]))
-        for i in range(moe.NUM_STAGE_EVENTS - 1):
-            f = ctypes.c_float()
-            H_.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(evs[i]),
-                                   ctypes.c_void_p(evs[i + 1]))
-            stage_ms[i] += f.value
+        stage_ms += [elapsed_ms(evs[i], evs[i + 1]) for i in range(moe.NUM_STAGE_EVENTS - 1)]
     stage_ms /= reps
-    for e in evs:
+    for e in evs + [e for p in pairs for e in p]:
         H_.hipEventDestroy(ctypes.c_void_p(e))
-    active, layer_bytes, flops, w13_bytes = algorithmic(spec, counts)
-    w13_ms = stage_ms[4]
+
+    active, layer_bytes, flops, w13_bytes, w13_flops = algorithmic(spec, counts)
     w13_gbs = w13_bytes / (w13_ms * 1e-3) / 1e9
+    peak_tf = MFMA_PEAK_TFLOPS[mode]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -202,19 +257,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[mode],
-        "data": "synthetic (seeded, moe_workloads recipe)",
+        "data": "synthetic (seeded; moe_workloads recipe)",
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d I=%d" % (
             spec.name, spec.T, spec.H, spec.E, spec.k, spec.I), "T": spec.T, "H": spec.H,
             "E": spec.E, "k": spec.k, "I": spec.I, "active_experts": active},
         "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
+        "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_tf,
+        "layer_alg_bytes": layer_bytes,
         "stage_ms": {n: round(float(v), 5) for n, v in zip(
             ["gating", "align_sort", "tiles", "x_quant", "w13_swiglu", "h_quant", "w2",
              "combine"], stage_ms)},
-        "roofline": {"bound": "hbm", "kernel": "w13_swiglu_skinny", "achieved": w13_gbs,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": w13_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": w13_bytes, "avg_ms": float(w13_ms)},
+                     "traffic": traffic_for(spec.name, kernel, big),
+                     "bytes_per_launch": w13_bytes, "avg_ms": w13_ms,
+                     "mfma_tflops": w13_flops / (w13_ms * 1e-3) / 1e12,
+                     "mfma_peak_tflops": peak_tf},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

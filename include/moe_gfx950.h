@@ -147,13 +147,19 @@ int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, co
                       void* stream);
 
 /* Stage timing for profiling: identical to moe_fused_forward, and in
- * addition records events[i] (each a hipEvent_t created by the caller) on
- * `stream` at stage boundary i, so that the elapsed time between
- * consecutive events is the time of one stage:
+ * addition takes timestamps into events[i] (a hipEvent_t created by the
+ * caller, or NULL to skip that point) at stage boundary i, so that the
+ * elapsed time between two of them is the time of the stages between:
  *   0 before gating | 1 after gating | 2 after grouping | 3 after the tile
- *   list | 4 after x quantisation (FP8; else same point as 3) | 5 after the
- *   gate/up GEMM | 6 after h quantisation (FP8; else same as 5) | 7 after
- *   the down GEMM | 8 after the aggregation.
+ *   list | 4 start of the gate/up GEMM kernel | 5 its end | 6 start of the
+ *   down GEMM kernel | 7 its end | 8 after the aggregation.
+ * Boundaries 4-7 are the GEMM kernels' own start and end times (attached to
+ * their dispatches, no marker packets around them), so 4->5 and 6->7 are
+ * exactly those kernels' durations; 3->4 holds the FP8 x quantisation and
+ * 5->6 the FP8 h quantisation.  The others are marker events on `stream`.
+ * For few-token batches (few pairs per expert and T*k <= 256) one kernel
+ * runs gating, grouping, the tile list and the x quantisation, so
+ * boundaries 1 to 3 fall at the same point after it.
  * n_events must be MOE_NUM_STAGE_EVENTS. */
 #define MOE_NUM_STAGE_EVENTS 9
 int moe_fused_forward_events(const moe_shape* s, const void* x, const float* logits,

@@ -212,7 +212,8 @@ def moe_fused_forward(x, logits, w13, w13_scale, w2, w2_scale, k, renormalize=Tr
 def moe_fused_forward_events(x, logits, w13, w13_scale, w2, w2_scale, k, events, renormalize=True,
                              out=None, ws=None, topk_ids=None, topk_weights=None):
     """moe_fused_forward that also records the given hipEvent_t handles
-    (NUM_STAGE_EVENTS integers) at the stage boundaries."""
+    (NUM_STAGE_EVENTS integers, 0 or None to skip a boundary) at the stage
+    boundaries."""
     mode = mode_of(w13)
     T, H = x.shape
     E, I2, _ = w13.shape
@@ -221,7 +222,7 @@ def moe_fused_forward_events(x, logits, w13, w13_scale, w2, w2_scale, k, events,
     ws = workspace(shape, x.device) if ws is None else ws
     if out is None:
         out = torch.empty((T, H), dtype=act_dtype(mode), device=x.device)
-    ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+    ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e or None) for e in events])
     _check(lib().moe_fused_forward_events(ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w13),
                                           _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
                                           _ptr(topk_ids), _ptr(topk_weights), _ptr(ws), ws.numel(),

@@ -48,6 +48,12 @@ inline bool use_tiles(const moe_shape& s) {
 }
 inline int tiles_bm(const moe_shape& s) { return (long)s.T * s.k < 64L * s.E ? 64 : 128; }
 
+// Few-token launch shortcut of the fused entry point: one block runs gating,
+// grouping, the tile list and the x quantisation up to kRouteSmallMax pairs.
+inline bool route_small(const moe_shape& s) {
+  return !use_tiles(s) && (long)s.T * s.k <= kRouteSmallMax;
+}
+
 Layout layout_for(const moe_shape& s) {
   Layout L;
   const long np = (long)s.T * s.k;
@@ -205,11 +211,11 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
   if (big)
     MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), b, w13, w13_scale, sorted_ids, tiles_big,
                              &ctrl->num_tiles_big, (int)L.max_tiles_big, s->H, s->I, s->k,
-                             &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, st));
+                             &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, nullptr, nullptr, st));
   else
     MOE_TRY(launch_w13_swiglu(s->wdtype, b, w13, w13_scale, sorted_ids, tiles, ctrl,
                               (int)L.max_tiles, s->H, s->I, s->k, &ctrl->amax_x_bits, h,
-                              &ctrl->amax_h_bits, st));
+                              &ctrl->amax_h_bits, nullptr, nullptr, st));
   if (fp8) MOE_TRY(launch_write_scales(ctrl, act_scales, st));
   return MOE_OK;
 }
@@ -249,10 +255,10 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   }
   if (big)
     MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), b, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
-                            (int)L.max_tiles_big, s->H, s->I, amax_h, y, st));
+                            (int)L.max_tiles_big, s->H, s->I, amax_h, y, nullptr, nullptr, st));
   else
     MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I,
-                      amax_h, y, st));
+                      amax_h, y, nullptr, nullptr, st));
   return MOE_OK;
 }
 
@@ -290,8 +296,13 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
     return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // boundaries 0-3 and 8 are marker events; 4/5 and 6/7 are the start / end
+  // of the gate/up and down GEMM dispatches themselves
+  auto ev = [&](int i) -> hipEvent_t {
+    return events ? reinterpret_cast<hipEvent_t>(events[i]) : nullptr;
+  };
   auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) : hipSuccess;
+    return ev(i) ? hipEventRecord(ev(i), st) : hipSuccess;
   };
   const Layout L = layout_for(*s);
   const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I;
@@ -308,35 +319,41 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   void* h = at<void>(ws, L.h);
   float* y = at<float>(ws, L.y);
 
+  const bool small = route_small(*s);
+  uint8_t* xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
+  const void* bx = fp8 ? static_cast<const void*>(xq) : x;
+
   MOE_TRY(mark(0));
-  MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
-                             reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
-  MOE_TRY(mark(1));
-  MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
-  MOE_TRY(mark(2));
-  if (big)
-    MOE_TRY(launch_build_tiles(offsets, E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
-  else
-    MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
-  MOE_TRY(mark(3));
-  const void* bx = x;
-  if (fp8) {
-    uint8_t* xq = at<uint8_t>(ws, L.xq);
-    if ((rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,
+  if (small) {
+    MOE_TRY(launch_route_small(logits, T, E, k, s->renormalize, ids, wts, counts, offsets, sorted,
+                               inv, kSkinnyBM, tiles, ctrl, reinterpret_cast<const uint16_t*>(x),
+                               H, xq, st));
+    for (int i = 1; i <= 3; i++) MOE_TRY(mark(i));
+  } else {
+    // zeroes the control block
+    MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
+                               reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
+    MOE_TRY(mark(1));
+    MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
+    MOE_TRY(mark(2));
+    if (big)
+      MOE_TRY(launch_build_tiles(offsets, E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
+    else
+      MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
+    MOE_TRY(mark(3));
+    if (fp8 &&
+        (rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,
                             xq, st)))
       return rc;
-    bx = xq;
   }
-  MOE_TRY(mark(4));
   if (big)
-    MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), bx, w13, w13_scale, sorted, tiles_big, &ctrl->num_tiles_big,
-                             (int)L.max_tiles_big, H, I, k, &ctrl->amax_x_bits, h,
-                             &ctrl->amax_h_bits, st));
+    MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), bx, w13, w13_scale, sorted, tiles_big,
+                             &ctrl->num_tiles_big, (int)L.max_tiles_big, H, I, k,
+                             &ctrl->amax_x_bits, h, &ctrl->amax_h_bits, ev(4), ev(5), st));
   else
     MOE_TRY(launch_w13_swiglu(s->wdtype, bx, w13, w13_scale, sorted, tiles, ctrl,
                               (int)L.max_tiles, H, I, k, &ctrl->amax_x_bits, h,
-                              &ctrl->amax_h_bits, st));
-  MOE_TRY(mark(5));
+                              &ctrl->amax_h_bits, ev(4), ev(5), st));
   const void* bh = h;
   if (fp8) {
     uint8_t* hq = at<uint8_t>(ws, L.hq);
@@ -344,14 +361,13 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
                               &ctrl->amax_h_bits, hq, st));
     bh = hq;
   }
-  MOE_TRY(mark(6));
   if (big)
-    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), bh, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
-                            (int)L.max_tiles_big, H, I, &ctrl->amax_h_bits, y, st));
+    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), bh, w2, w2_scale, tiles_big,
+                            &ctrl->num_tiles_big, (int)L.max_tiles_big, H, I, &ctrl->amax_h_bits,
+                            y, ev(6), ev(7), st));
   else
     MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,
-                      &ctrl->amax_h_bits, y, st));
-  MOE_TRY(mark(7));
+                      &ctrl->amax_h_bits, y, ev(6), ev(7), st));
   MOE_TRY(launch_combine(s->wdtype, y, inv, wts, T, H, k, out, st));
   MOE_TRY(mark(8));
   return MOE_OK;
@@ -375,8 +391,6 @@ int moe_fused_forward_events(const moe_shape* s, const void* x, const float* log
                              float* topk_weights, void* ws, size_t ws_bytes, void* stream,
                              void** events, int32_t n_events) {
   if (!events || n_events != MOE_NUM_STAGE_EVENTS) return MOE_ERR_INVALID_ARG;
-  for (int i = 0; i < n_events; i++)
-    if (!events[i]) return MOE_ERR_INVALID_ARG;
   return fused_impl(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
                     ws_bytes, stream, events);
 }

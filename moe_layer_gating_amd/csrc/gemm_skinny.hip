@@ -286,54 +286,60 @@ template <int MODE>
 static void launch_w13_mode(long max_tiles, const char* b, const char* w13, const float* w13_scale,
                             const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl, int H,
                             int I, int k, const uint32_t* act_amax_bits, void* h,
-                            uint32_t* amax_h_bits, hipStream_t st) {
+                            uint32_t* amax_h_bits, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
   constexpr int KS = ksplit_w13<MODE>();
   const long blocks = max_tiles * (I / (8 * (4 / KS)));
-  w13_swiglu_skinny<MODE, KS><<<blocks, 256, 0, st>>>(b, w13, w13_scale, sorted_ids, tiles, ctrl, H,
-                                                      I, k, act_amax_bits, h, amax_h_bits);
+  launch_on(w13_swiglu_skinny<MODE, KS>, dim3(blocks), dim3(256), st, e0, e1, b, w13, w13_scale,
+            sorted_ids, tiles, ctrl, H, I, k, act_amax_bits, h, amax_h_bits);
 }
 
 template <int MODE>
 static void launch_w2_mode(long max_tiles, const char* b, const char* w2, const float* w2_scale,
                            const Tile* tiles, const Ctrl* ctrl, int H, int I,
-                           const uint32_t* act_amax_bits, float* y, hipStream_t st) {
+                           const uint32_t* act_amax_bits, float* y, hipEvent_t e0, hipEvent_t e1,
+                           hipStream_t st) {
   constexpr int KS = ksplit_w2<MODE>();
   const long blocks = max_tiles * (H / (16 * (4 / KS)));
-  w2_skinny<MODE, KS><<<blocks, 256, 0, st>>>(b, w2, w2_scale, tiles, ctrl, H, I, act_amax_bits, y);
+  launch_on(w2_skinny<MODE, KS>, dim3(blocks), dim3(256), st, e0, e1, b, w2, w2_scale, tiles, ctrl,
+            H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const float* w13_scale,
                              const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl,
                              int max_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
-                             void* h, uint32_t* amax_h_bits, hipStream_t st) {
+                             void* h, uint32_t* amax_h_bits, hipEvent_t e0, hipEvent_t e1,
+                             hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w13);
   if (mode == MOE_F32)
     launch_w13_mode<MOE_F32>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
-                             act_amax_bits, h, amax_h_bits, st);
+                             act_amax_bits, h, amax_h_bits, e0, e1, st);
   else if (mode == MOE_BF16)
     launch_w13_mode<MOE_BF16>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
-                              act_amax_bits, h, amax_h_bits, st);
+                              act_amax_bits, h, amax_h_bits, e0, e1, st);
   else
     launch_w13_mode<MOE_FP8_E4M3>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
-                                  act_amax_bits, h, amax_h_bits, st);
+                                  act_amax_bits, h, amax_h_bits, e0, e1, st);
   return hipGetLastError();
 }
 
 hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
                      const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
-                     const uint32_t* act_amax_bits, float* y, hipStream_t st) {
+                     const uint32_t* act_amax_bits, float* y, hipEvent_t e0, hipEvent_t e1,
+                     hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w2);
   if (mode == MOE_F32)
-    launch_w2_mode<MOE_F32>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, st);
+    launch_w2_mode<MOE_F32>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, e0,
+                            e1, st);
   else if (mode == MOE_BF16)
-    launch_w2_mode<MOE_BF16>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, st);
+    launch_w2_mode<MOE_BF16>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y, e0,
+                             e1, st);
   else
     launch_w2_mode<MOE_FP8_E4M3>(max_tiles, bb, ww, w2_scale, tiles, ctrl, H, I, act_amax_bits, y,
-                                 st);
+                                 e0, e1, st);
   return hipGetLastError();
 }
 

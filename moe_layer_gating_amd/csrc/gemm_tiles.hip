@@ -309,34 +309,34 @@ static void launch_tiles_w13_mode(long max_tiles, const char* b, const char* w13
                                   const float* w13_scale, const int32_t* sorted_ids,
                                   const Tile* tiles, const int32_t* num_tiles, int H, int I, int k,
                                   const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
-                                  hipStream_t st) {
+                                  hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
   const long blocks = max_tiles * (2L * I / kTileN);
-  w13_swiglu_tiles<MODE, BM><<<blocks, 256, 0, st>>>(b, w13, w13_scale, sorted_ids, tiles,
-                                                     num_tiles, H, I, k, act_amax_bits, h,
-                                                     amax_h_bits);
+  launch_on(w13_swiglu_tiles<MODE, BM>, dim3(blocks), dim3(256), st, e0, e1, b, w13, w13_scale,
+            sorted_ids, tiles, num_tiles, H, I, k, act_amax_bits, h, amax_h_bits);
 }
 
 template <int MODE, int BM>
 static void launch_tiles_w2_mode(long max_tiles, const char* b, const char* w2,
                                  const float* w2_scale, const Tile* tiles,
                                  const int32_t* num_tiles, int H, int I,
-                                 const uint32_t* act_amax_bits, float* y, hipStream_t st) {
+                                 const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
+                                 hipEvent_t e1, hipStream_t st) {
   const long blocks = max_tiles * (long)(H / kTileN);
-  w2_tiles<MODE, BM><<<blocks, 256, 0, st>>>(b, w2, w2_scale, tiles, num_tiles, H, I,
-                                             act_amax_bits, y);
+  launch_on(w2_tiles<MODE, BM>, dim3(blocks), dim3(256), st, e0, e1, b, w2, w2_scale, tiles,
+            num_tiles, H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
                             const float* w13_scale, const int32_t* sorted_ids, const Tile* tiles,
                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                             const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
-                            hipStream_t st) {
+                            hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w13);
 #define MOE_W13_TILES(MODE_, BM_)                                                             \
   launch_tiles_w13_mode<MODE_, BM_>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, num_tiles, \
-                                    H, I, k, act_amax_bits, h, amax_h_bits, st)
+                                    H, I, k, act_amax_bits, h, amax_h_bits, e0, e1, st)
   if (mode == MOE_BF16 && bm == 64)
     MOE_W13_TILES(MOE_BF16, 64);
   else if (mode == MOE_BF16 && bm == 128)
@@ -353,13 +353,14 @@ hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
 
 hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, const float* w2_scale,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
-                           int I, const uint32_t* act_amax_bits, float* y, hipStream_t st) {
+                           int I, const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
+                           hipEvent_t e1, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w2);
 #define MOE_W2_TILES(MODE_, BM_)                                                                \
   launch_tiles_w2_mode<MODE_, BM_>(max_tiles, bb, ww, w2_scale, tiles, num_tiles, H, I,         \
-                                   act_amax_bits, y, st)
+                                   act_amax_bits, y, e0, e1, st)
   if (mode == MOE_BF16 && bm == 64)
     MOE_W2_TILES(MOE_BF16, 64);
   else if (mode == MOE_BF16 && bm == 128)

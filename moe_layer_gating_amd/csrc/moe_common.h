@@ -2,6 +2,7 @@
 // the HIP translation units of the fused MoE library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,6 +12,7 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kSkinnyBM = 16;  // sorted positions per tile of the few-token GEMMs
+constexpr int kRouteSmallMax = 256;  // pairs routed by the one-block front kernel
 constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -78,6 +80,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Launch `kern` on `st`; when e0 / e1 are given they take the kernel's own
+// start / end time (hipExtLaunchKernelGGL), which is how the stage-timing
+// entry point times the GEMMs without marker packets around them.
+template <typename... KArgs, typename... Args>
+inline void launch_on(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t e0,
+                      hipEvent_t e1, Args... args) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, st, e0, e1, 0, static_cast<KArgs>(args)...);
+  else
+    kern<<<grid, block, 0, st>>>(static_cast<KArgs>(args)...);
+}
+
 // --------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All work goes to `st`.
 hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
@@ -85,6 +99,13 @@ hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int reno
 hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
                              hipStream_t st);
+// Gating, grouping, tile list and (xq != nullptr) FP8 quantisation of x in
+// one block, for T*k <= kRouteSmallMax; inv_perm may be null.  Writes every
+// control word.
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                              float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                              int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
+                              const uint16_t* x, int H, uint8_t* xq, hipStream_t st);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
                               int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
@@ -98,20 +119,23 @@ hipError_t launch_write_scales(const Ctrl* ctrl, float* act_scales, hipStream_t 
 hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const float* w13_scale,
                              const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl,
                              int max_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
-                             void* h, uint32_t* amax_h_bits, hipStream_t st);
+                             void* h, uint32_t* amax_h_bits, hipEvent_t e0, hipEvent_t e1,
+                             hipStream_t st);
 hipError_t launch_w2(int mode, const void* b, const void* w2, const float* w2_scale,
                      const Tile* tiles, const Ctrl* ctrl, int max_tiles, int H, int I,
-                     const uint32_t* act_amax_bits, float* y, hipStream_t st);
+                     const uint32_t* act_amax_bits, float* y, hipEvent_t e0, hipEvent_t e1,
+                     hipStream_t st);
 // Many-token variants (bf16 and FP8 only; tiles of bm = 64 or 128 sorted
 // positions); the tile count is read from *num_tiles on the device.
 hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
                             const float* w13_scale, const int32_t* sorted_ids, const Tile* tiles,
                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                             const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
-                            hipStream_t st);
+                            hipEvent_t e0, hipEvent_t e1, hipStream_t st);
 hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, const float* w2_scale,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
-                           int I, const uint32_t* act_amax_bits, float* y, hipStream_t st);
+                           int I, const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
+                           hipEvent_t e1, hipStream_t st);
 hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,
                           int H, int k, void* out, hipStream_t st);
 

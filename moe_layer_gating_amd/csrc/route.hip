@@ -27,16 +27,12 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restrict__ logits, int T,
-                                                          int E, int k, int renorm,
-                                                          int32_t* __restrict__ ids,
-                                                          float* __restrict__ wts,
-                                                          uint32_t* zero_words, int n_zero) {
-  if (blockIdx.x == 0 && (int)threadIdx.x < n_zero) zero_words[threadIdx.x] = 0u;
+// Top-k of one token by one whole wave; lanes 0..k-1 write slot `lane` to
+// ids_row / wts_row (and to lds_ids if given).
+__device__ __forceinline__ void gate_token(const float* __restrict__ row, int E, int k, int renorm,
+                                           int32_t* __restrict__ ids_row,
+                                           float* __restrict__ wts_row, int* lds_ids) {
   const int lane = lane_id();
-  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
   float v[kMaxPerLane];
   const int per_lane = (E + kWave - 1) / kWave;
 #pragma unroll
@@ -94,9 +90,23 @@ __global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restric
     denom = wave_sum(s);
   }
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    wts[(size_t)t * k + lane] = ex / denom;
+    ids_row[lane] = my_e;
+    wts_row[lane] = ex / denom;
+    if (lds_ids) lds_ids[lane] = my_e;
   }
+}
+
+__global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int k, int renorm,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ wts,
+                                                          uint32_t* zero_words, int n_zero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  gate_token(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k,
+             nullptr);
 }
 
 hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
@@ -261,6 +271,174 @@ __global__ void zero_words_kernel(uint32_t* p, int n) {
 
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
   zero_words_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- small batches
+// Exclusive scan of one int per thread over a 1024-thread block; returns the
+// prefix and writes the block total to *total.  `tmp` holds 16 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int* total) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int nb = __shfl_up(incl, o);
+    if (lane >= o) incl += nb;
+  }
+  if (lane == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    int c = tmp[i];
+    if (i < w) base += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// The whole front of the layer for a small batch (T*k <= kRouteSmallMax
+// pairs) in one block of 16 waves, so that a decode step pays one launch for
+// it instead of one per stage:
+//   1. top-k gating, one wave per token;
+//   2. expert histogram (LDS integer atomics: counts do not depend on order)
+//      and its exclusive scan -> counts, offsets; thread e owns expert e;
+//   3. the list of tiles of <= bm positions;
+//   4. stable grouping: pair f lands at its expert's offset plus the number
+//      of earlier pairs routed to the same expert, so pairs keep ascending
+//      order inside each expert;
+//   5. FP8 (xq != nullptr): amax(x) over the block and the e4m3 codes of x.
+// Every control word is written here: amax_x (0 unless FP8), amax_h = 0 and
+// the tile counts.
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ inv_perm, int bm,
+    Tile* __restrict__ tiles, Ctrl* ctrl, const uint16_t* __restrict__ x, int H,
+    uint8_t* __restrict__ xq) {
+  constexpr int NW = 16;
+  __shared__ int s_ids[kRouteSmallMax];
+  __shared__ int hist[1024];
+  __shared__ int run[1024];  // offsets of the experts
+  __shared__ int tmp[NW];
+  __shared__ float red[NW];
+  const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+  const int n = T * k;
+  hist[t] = 0;
+
+  // 1. gating
+  for (int tok = w; tok < T; tok += NW)
+    gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
+               wts + (size_t)tok * k, s_ids + tok * k);
+  __syncthreads();
+
+  // 2. histogram and scans of the counts and of the tile counts
+  for (int f = t; f < n; f += 1024) atomicAdd(&hist[s_ids[f]], 1);
+  __syncthreads();
+  const int cnt = (t < E) ? hist[t] : 0;
+  const int nt = (cnt + bm - 1) / bm;
+  int total_pairs, total_tiles;
+  const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
+  const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
+  if (t < E) {
+    counts[t] = cnt;
+    offsets[t] = pre;
+    run[t] = pre;
+    // 3. tiles of this expert
+    for (int i = 0; i < nt; i++) {
+      Tile tl;
+      tl.e = t;
+      tl.p0 = pre + i * bm;
+      tl.mt = min(bm, cnt - i * bm);
+      tl.pad = 0;
+      tiles[tpre + i] = tl;
+    }
+  }
+  if (t == 0) offsets[E] = n;
+  __syncthreads();
+
+  // 4. stable grouping: pair f goes to its expert's offset plus the number of
+  // earlier pairs on the same expert (broadcast LDS reads, no atomics)
+  for (int f = t; f < n; f += 1024) {
+    const int e = s_ids[f];
+    int rank = 0;
+    for (int j = 0; j < f; j++) rank += (s_ids[j] == e);
+    const int pos = run[e] + rank;
+    sorted_ids[pos] = f;
+    if (inv_perm) inv_perm[f] = pos;
+  }
+
+  // 5. FP8 activation quantisation (x is bf16, H a multiple of 128): four
+  // 16-byte loads in flight per thread
+  uint32_t amax_bits = 0u;
+  if (xq) {
+    const int n8 = T * H / 8;
+    const i32x4* x4 = reinterpret_cast<const i32x4*>(x);
+    float m = 0.f;
+    for (int i0 = t; i0 < n8; i0 += 4 * 1024) {
+      i32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int i = i0 + u * 1024;
+        v[u] = (i < n8) ? x4[i] : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint32_t uu = (uint32_t)v[u][q];
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(uu & 0xffffu))));
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(uu >> 16))));
+        }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; i++) a = fmaxf(a, red[i]);
+    amax_bits = __float_as_uint(a);
+    const float r = a > 0.f ? 448.0f / a : 1.0f;
+    uint2* d2 = reinterpret_cast<uint2*>(xq);
+    for (int i0 = t; i0 < n8; i0 += 4 * 1024) {
+      i32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int i = i0 + u * 1024;
+        v[u] = (i < n8) ? x4[i] : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int i = i0 + u * 1024;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+          const uint32_t u0 = (uint32_t)v[u][q], u2 = (uint32_t)v[u][q + 2];
+          lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u0 & 0xffffu)) * r) << (16 * q);
+          lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u0 >> 16)) * r) << (16 * q + 8);
+          hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 & 0xffffu)) * r) << (16 * q);
+          hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 >> 16)) * r) << (16 * q + 8);
+        }
+        if (i < n8) d2[i] = make_uint2(lo, hi);
+      }
+    }
+  }
+  if (t == 0) {
+    ctrl->amax_x_bits = amax_bits;
+    ctrl->amax_h_bits = 0u;
+    ctrl->num_tiles = total_tiles;
+    ctrl->num_tiles_big = 0;
+  }
+}
+
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                              float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                              int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
+                              const uint16_t* x, int H, uint8_t* xq, hipStream_t st) {
+  route_small_kernel<<<1, 1024, 0, st>>>(logits, T, E, k, renorm, ids, w, counts, offsets,
+                                         sorted_ids, inv_perm, bm, tiles, ctrl, x, H, xq);
   return hipGetLastError();
 }
 
