@@ -42,6 +42,11 @@ CASES = [
     ("fp8_empty", 40, 384, 20, 4, 256, FP8, "empty"),
     ("fp8_t1", 1, 512, 64, 8, 256, FP8, "uniform"),
     ("fp8_k_equals_E", 6, 256, 4, 4, 128, FP8, "uniform"),
+    # few pairs per expert with more than 256 pairs: the multi-kernel front
+    # (gating, grouping and tile-list kernels) instead of the one-block one
+    ("fp8_skinny_many_pairs", 40, 256, 64, 8, 256, FP8, "uniform"),
+    ("bf16_skinny_t100", 100, 256, 16, 2, 256, BF16, "uniform"),
+    ("bf16_skinny_t200", 200, 256, 32, 2, 128, BF16, "uniform"),
     # many pairs per expert: the 128-position tiled GEMMs (several tiles per
     # expert, ragged last tiles, 8+ weight-row blocks, empty and skewed experts)
     ("fp8_tiles_ragged", 600, 512, 8, 2, 512, FP8, "uniform"),
