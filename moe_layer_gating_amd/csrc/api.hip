@@ -34,7 +34,8 @@ inline long max_tiles_for(long n_pairs, int E, int bm) {
 
 // Offsets of the workspace regions for one shape.
 struct Layout {
-  size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, tiles_big, xq, hq, h, y, total;
+  size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, tiles_big, chunk_counts, chunk_base,
+      rank, xq, hq, h, y, total;
   long max_tiles, max_tiles_big;
 };
 
@@ -74,6 +75,10 @@ Layout layout_for(const moe_shape& s) {
   L.inv = take(np * 4);
   L.tiles = take((size_t)(L.max_tiles + 1) * sizeof(Tile));
   L.tiles_big = take((size_t)(L.max_tiles_big + 1) * sizeof(Tile));
+  const size_t n_chunks = (np + kSortChunk - 1) / kSortChunk;
+  L.chunk_counts = take(n_chunks * s.E * 4);
+  L.chunk_base = take(n_chunks * s.E * 4);
+  L.rank = take(np * 4);
   const bool fp8 = s.wdtype == MOE_FP8_E4M3;
   L.xq = take(fp8 ? (size_t)s.T * s.H : 0);
   L.hq = take(fp8 ? (size_t)np * s.I : 0);
@@ -334,12 +339,19 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
     MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
                                reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
     MOE_TRY(mark(1));
-    MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
-    MOE_TRY(mark(2));
-    if (big)
-      MOE_TRY(launch_build_tiles(offsets, E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
-    else
-      MOE_TRY(launch_build_tiles(offsets, E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
+    const int bm = big ? tiles_bm(*s) : kSkinnyBM;
+    Tile* tl = big ? tiles_big : tiles;
+    int32_t* nt = big ? &ctrl->num_tiles_big : &ctrl->num_tiles;
+    if ((long)T * k >= kChunkSortMin) {
+      MOE_TRY(launch_chunk_sort(ids, T * k, E, counts, offsets, sorted, inv, bm, tl, nt,
+                                at<int32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.chunk_base),
+                                at<int32_t>(ws, L.rank), st));
+      MOE_TRY(mark(2));
+    } else {
+      MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
+      MOE_TRY(mark(2));
+      MOE_TRY(launch_build_tiles(offsets, E, bm, tl, nt, st));
+    }
     MOE_TRY(mark(3));
     if (fp8 &&
         (rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,

@@ -14,9 +14,9 @@
 //
 // Work decomposition: a row group is 16 weight rows of one expert for one
 // tile of <= 16 sorted positions (one entry of the tile list), over the whole
-// reduction dimension K.  A block of 4 waves takes 4/KSPLIT row groups; the
-// KSPLIT waves of a group split K and add their 16x16 partial products
-// through LDS in a fixed order.  The epilogue then forms
+// reduction dimension K.  A block's NW waves all take the same row group and
+// split K; their 16x16 partial products are added through LDS in a fixed
+// order.  The epilogue then forms
 //   w13: the SwiGLU h = silu(c*g) * (c*u) (gate and up rows interleaved);
 //   w2 : 16 output features of y, scaled by the FP8 dequantisation factor.
 // Scales are applied to the fp32 accumulators in the epilogue (agentic-
@@ -139,22 +139,21 @@ __device__ __forceinline__ float act_scale_from_bits(const uint32_t* bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
-// Sum the KSPLIT partial 16x16 products of the waves that share a row group,
-// in a fixed order (wave 0 of the group first).  Every lane of the first wave
-// of a group gets its own 4 accumulator entries back; the other waves'
-// results are unspecified.  KSPLIT = 1 needs no exchange.
-template <int KSPLIT>
-__device__ __forceinline__ f32x4 group_reduce(f32x4 acc, float (*red)[64][4]) {
-  if (KSPLIT == 1) return acc;
+// Sum the NW partial 16x16 products of the block's waves in a fixed order
+// ((w0 + w1) + w2) + ...; the result is valid in wave 0 only.
+template <int NW>
+__device__ __forceinline__ f32x4 block_reduce(f32x4 acc, float (*red)[64][4]) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
+  if (w > 0) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) red[w][lane][i] = acc[i];
+    for (int i = 0; i < 4; i++) red[w - 1][lane][i] = acc[i];
+  }
   __syncthreads();
-  if (w % KSPLIT == 0) {
+  if (w == 0) {
 #pragma unroll
-    for (int q = 1; q < KSPLIT; q++)
+    for (int q = 1; q < NW; q++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[i] += red[w + q][lane][i];
+      for (int i = 0; i < 4; i++) acc[i] += red[q - 1][lane][i];
   }
   return acc;
 }
@@ -168,29 +167,27 @@ __device__ __forceinline__ void amax_update(uint32_t* amax_bits, float v) {
 }
 
 // ------------------------------------------------------------------- w13
-// Block = 4 waves = 4/KSPLIT row groups, each split over K by KSPLIT waves.
-// A row group is 8 gate rows n0..n0+7 and the 8 matching up rows, interleaved
-// on the MFMA row side: MFMA row 2i is gate row n0+i, row 2i+1 up row I+n0+i.
-// The accumulator rows a lane holds (4g..4g+3) are then gate/up/gate/up of
-// features n0+2g and n0+2g+1, so the SwiGLU is formed inside the lane.
-template <int MODE, int KSPLIT, int U = unroll_for<MODE>()>
-__global__ __launch_bounds__(256) void w13_swiglu_skinny(
+// Block = NW waves on one row group of 8 gate rows n0..n0+7 and the 8
+// matching up rows, interleaved on the MFMA row side: MFMA row 2i is gate row
+// n0+i, row 2i+1 up row I+n0+i.  The accumulator rows a lane holds
+// (4g..4g+3) are then gate/up/gate/up of features n0+2g and n0+2g+1, so the
+// SwiGLU is formed inside the lane.  The NW waves split K.
+template <int MODE, int NW, int U = unroll_for<MODE>()>
+__global__ __launch_bounds__(NW * 64) void w13_swiglu_skinny(
     const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
     const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
     const Ctrl* __restrict__ ctrl, int H, int I, int k, const uint32_t* act_amax_bits,
     void* __restrict__ h, uint32_t* amax_h_bits) {
   typedef Step<MODE> S;
-  constexpr int RG = 4 / KSPLIT;
-  __shared__ float red[KSPLIT > 1 ? 4 : 1][64][4];
-  const int blocks_per_tile = I / (8 * RG);
+  __shared__ float red[NW - 1][64][4];
+  const int blocks_per_tile = I / 8;
   const int tile_idx = blockIdx.x / blocks_per_tile;
   const int rb = blockIdx.x - tile_idx * blocks_per_tile;
   if (tile_idx >= ctrl->num_tiles) return;
   const Tile tl = tiles[tile_idx];
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = (rb * RG + w / KSPLIT) * 8;
-  const int kp = w % KSPLIT;
+  const int n0 = rb * 8;
   const int wrow = (r & 1) ? (I + n0 + (r >> 1)) : (n0 + (r >> 1));
   const char* arow = w13 + ((size_t)tl.e * 2 * I + wrow) * (size_t)H * S::ES;
   const char* brow = nullptr;
@@ -199,10 +196,10 @@ __global__ __launch_bounds__(256) void w13_swiglu_skinny(
     brow = b + (size_t)tok * H * S::ES;
   }
   const int n_steps = H / S::KS;
-  const int s0 = (kp * n_steps) / KSPLIT, s1 = ((kp + 1) * n_steps) / KSPLIT;
+  const int s0 = (w * n_steps) / NW, s1 = ((w + 1) * n_steps) / NW;
   f32x4 acc = wave_dot<MODE, U>(arow, brow, s0, s1, g);
-  acc = group_reduce<KSPLIT>(acc, red);
-  if (kp != 0) return;
+  acc = block_reduce<NW>(acc, red);
+  if (w != 0) return;
 
   float c = 1.0f;
   if (MODE == MOE_FP8_E4M3) c = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
@@ -235,51 +232,249 @@ __global__ __launch_bounds__(256) void w13_swiglu_skinny(
 }
 
 // -------------------------------------------------------------------- w2
-// Block = 4/KSPLIT row groups of 16 output features m0..m0+15, each split over
-// K by KSPLIT waves.  A lane's accumulator rows 4g..4g+3 are 4 consecutive
-// features of its token column: one 16-byte store of y.
-template <int MODE, int KSPLIT, int U = unroll_for<MODE>()>
-__global__ __launch_bounds__(256) void w2_skinny(const char* __restrict__ b,
-                                                 const char* __restrict__ w2,
-                                                 const float* __restrict__ w2_scale,
-                                                 const Tile* __restrict__ tiles,
-                                                 const Ctrl* __restrict__ ctrl, int H, int I,
-                                                 const uint32_t* act_amax_bits,
-                                                 float* __restrict__ y) {
+// Block = NW waves on one row group of 16 output features m0..m0+15, splitting
+// K.  A lane's accumulator rows 4g..4g+3 are 4 consecutive features of its
+// token column: one 16-byte store of y.
+template <int MODE, int NW, int U = unroll_for<MODE>()>
+__global__ __launch_bounds__(NW * 64) void w2_skinny(const char* __restrict__ b,
+                                                     const char* __restrict__ w2,
+                                                     const float* __restrict__ w2_scale,
+                                                     const Tile* __restrict__ tiles,
+                                                     const Ctrl* __restrict__ ctrl, int H, int I,
+                                                     const uint32_t* act_amax_bits,
+                                                     float* __restrict__ y) {
   typedef Step<MODE> S;
-  constexpr int RG = 4 / KSPLIT;
-  __shared__ float red[KSPLIT > 1 ? 4 : 1][64][4];
-  const int blocks_per_tile = H / (16 * RG);
+  __shared__ float red[NW - 1][64][4];
+  const int blocks_per_tile = H / 16;
   const int tile_idx = blockIdx.x / blocks_per_tile;
   const int rb = blockIdx.x - tile_idx * blocks_per_tile;
   if (tile_idx >= ctrl->num_tiles) return;
   const Tile tl = tiles[tile_idx];
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int m0 = (rb * RG + w / KSPLIT) * 16;
-  const int kp = w % KSPLIT;
+  const int m0 = rb * 16;
   const char* arow = w2 + ((size_t)tl.e * H + m0 + r) * (size_t)I * S::ES;
   const char* brow = (r < tl.mt) ? b + (size_t)(tl.p0 + r) * I * S::ES : nullptr;
   const int n_steps = I / S::KS;
-  const int s0 = (kp * n_steps) / KSPLIT, s1 = ((kp + 1) * n_steps) / KSPLIT;
+  const int s0 = (w * n_steps) / NW, s1 = ((w + 1) * n_steps) / NW;
   f32x4 acc = wave_dot<MODE, U>(arow, brow, s0, s1, g);
-  acc = group_reduce<KSPLIT>(acc, red);
-  if (kp != 0 || r >= tl.mt) return;
+  acc = block_reduce<NW>(acc, red);
+  if (w != 0 || r >= tl.mt) return;
   if (MODE == MOE_FP8_E4M3) acc *= act_scale_from_bits(act_amax_bits) * w2_scale[tl.e];
   *reinterpret_cast<f32x4*>(y + (size_t)(tl.p0 + r) * H + m0 + 4 * g) = acc;
 }
 
-// Waves per row group that split the reduction dimension.  All four waves of
-// a block work on the same 16 rows: the block's concurrent loads then fall in
-// the same DRAM pages, which measured faster than giving each wave its own
-// rows for every decode shape.
+// ------------------------------------------------ several tiles per block
+// The same decomposition for tiles of up to 16*CT sorted positions: a block's
+// 4 waves split K over RT*16 weight rows, and every weight fragment a lane
+// loads feeds CT MFMAs (one per 16-token column tile), every token fragment
+// RT.  The K split keeps the block's concurrent weight loads inside the same
+// few rows (DRAM pages) as in the one-tile kernels.
+template <int MODE, int RT, int CT, int U>
+__device__ __forceinline__ void wave_dot_multi(const char* const* arow, const char* const* brow,
+                                               int s0, int s1, int g, f32x4 (*acc)[CT]) {
+  typedef Step<MODE> S;
+  constexpr int STEP_BYTES = S::KS * S::ES;
+  const int lane_off = g * S::LANE_K * S::ES;
+  int s = s0;
+  for (; s + U <= s1; s += U) {
+    typename S::Frag a[U][RT], b[U][CT];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int i = 0; i < RT; i++) a[u][i] = S::load(arow[i] + (size_t)(s + u) * STEP_BYTES + lane_off);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int j = 0; j < CT; j++)
+        b[u][j] = brow[j] ? S::load(brow[j] + (size_t)(s + u) * STEP_BYTES + lane_off) : S::zero();
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int i = 0; i < RT; i++)
+#pragma unroll
+        for (int j = 0; j < CT; j++) acc[i][j] = S::mma(a[u][i], b[u][j], acc[i][j]);
+  }
+  for (; s < s1; s++) {
+    typename S::Frag a[RT], b[CT];
+#pragma unroll
+    for (int i = 0; i < RT; i++) a[i] = S::load(arow[i] + (size_t)s * STEP_BYTES + lane_off);
+#pragma unroll
+    for (int j = 0; j < CT; j++)
+      b[j] = brow[j] ? S::load(brow[j] + (size_t)s * STEP_BYTES + lane_off) : S::zero();
+#pragma unroll
+    for (int i = 0; i < RT; i++)
+#pragma unroll
+      for (int j = 0; j < CT; j++) acc[i][j] = S::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Partials of the 4 waves: red[wave][tile][lane][4]; tile q = i*CT + j is
+// finished by wave q % 4 as ((w0 + w1) + w2) + w3.
+template <int RT, int CT>
+__device__ __forceinline__ void store_partials(f32x4 (*acc)[CT], float (*red)[RT * CT][64][4]) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < RT; i++)
+#pragma unroll
+    for (int j = 0; j < CT; j++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) red[w][i * CT + j][lane][v] = acc[i][j][v];
+}
+
+template <int RT, int CT>
+__device__ __forceinline__ f32x4 sum_partials(float (*red)[RT * CT][64][4], int q) {
+  const int lane = lane_id();
+  f32x4 v;
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+    v[c] = ((red[0][q][lane][c] + red[1][q][lane][c]) + red[2][q][lane][c]) + red[3][q][lane][c];
+  return v;
+}
+
+// w13: block = RT row groups of 8 gate + 8 up features (interleaved as in
+// w13_swiglu_skinny), n0 = first feature; token column c of a tile is its
+// sorted position p0 + c.
+template <int MODE, int RT, int CT, int U = unroll_for<MODE>()>
+__global__ __launch_bounds__(256) void w13_swiglu_wide(
+    const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
+    const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
+    void* __restrict__ h, uint32_t* amax_h_bits) {
+  typedef Step<MODE> S;
+  __shared__ float red[4][RT * CT][64][4];
+  const int blocks_per_tile = I / (8 * RT);
+  const int tile_idx = blockIdx.x / blocks_per_tile;
+  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
+  if (tile_idx >= *num_tiles) return;
+  const Tile tl = tiles[tile_idx];
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = rb * RT * 8;
+  const size_t row_bytes = (size_t)H * S::ES;
+  const char* arow[RT];
+#pragma unroll
+  for (int i = 0; i < RT; i++) {
+    const int f = n0 + i * 8 + (r >> 1);
+    arow[i] = w13 + ((size_t)tl.e * 2 * I + ((r & 1) ? I + f : f)) * row_bytes;
+  }
+  const char* brow[CT];
+#pragma unroll
+  for (int j = 0; j < CT; j++) {
+    const int col = j * 16 + r;
+    brow[j] = col < tl.mt ? b + (size_t)(sorted_ids[tl.p0 + col] / k) * row_bytes : nullptr;
+  }
+  f32x4 acc[RT][CT];
+#pragma unroll
+  for (int i = 0; i < RT; i++)
+#pragma unroll
+    for (int j = 0; j < CT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_steps = H / S::KS;
+  wave_dot_multi<MODE, RT, CT, U>(arow, brow, (w * n_steps) / 4, ((w + 1) * n_steps) / 4, g, acc);
+  store_partials<RT, CT>(acc, red);
+  __syncthreads();
+
+  float cs = 1.0f;
+  if (MODE == MOE_FP8_E4M3) cs = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
+  float hmax = 0.f;
+  for (int q = w; q < RT * CT; q += 4) {
+    const int i = q / CT, j = q % CT, col = j * 16 + r;
+    const f32x4 v = sum_partials<RT, CT>(red, q);
+    if (col < tl.mt) {
+      float hv[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; e2++) {
+        float gv = v[2 * e2], uv = v[2 * e2 + 1];
+        if (MODE == MOE_FP8_E4M3) {
+          gv *= cs;
+          uv *= cs;
+        }
+        hv[e2] = gv / (1.0f + expf(-gv)) * uv;
+      }
+      const size_t o = (size_t)(tl.p0 + col) * I + n0 + i * 8 + 2 * g;
+      if (MODE == MOE_F32) {
+        *reinterpret_cast<float2*>(reinterpret_cast<float*>(h) + o) = make_float2(hv[0], hv[1]);
+      } else {
+        const uint16_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(h) + o) =
+            (uint32_t)h0 | ((uint32_t)h1 << 16);
+        hmax = fmaxf(hmax, fmaxf(fabsf(bf16_to_f32(h0)), fabsf(bf16_to_f32(h1))));
+      }
+    }
+  }
+  if (MODE == MOE_FP8_E4M3) {
+    hmax = wave_max(hmax);
+    if (lane == 0) amax_update(amax_h_bits, hmax);
+  }
+}
+
+// w2: block = RT row groups of 16 output features starting at m0.
+template <int MODE, int RT, int CT, int U = unroll_for<MODE>()>
+__global__ __launch_bounds__(256) void w2_wide(const char* __restrict__ b,
+                                               const char* __restrict__ w2,
+                                               const float* __restrict__ w2_scale,
+                                               const Tile* __restrict__ tiles,
+                                               const int32_t* __restrict__ num_tiles, int H, int I,
+                                               const uint32_t* act_amax_bits,
+                                               float* __restrict__ y) {
+  typedef Step<MODE> S;
+  __shared__ float red[4][RT * CT][64][4];
+  const int blocks_per_tile = H / (16 * RT);
+  const int tile_idx = blockIdx.x / blocks_per_tile;
+  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
+  if (tile_idx >= *num_tiles) return;
+  const Tile tl = tiles[tile_idx];
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int m0 = rb * RT * 16;
+  const size_t row_bytes = (size_t)I * S::ES;
+  const char* arow[RT];
+#pragma unroll
+  for (int i = 0; i < RT; i++) arow[i] = w2 + ((size_t)tl.e * H + m0 + i * 16 + r) * row_bytes;
+  const char* brow[CT];
+#pragma unroll
+  for (int j = 0; j < CT; j++) {
+    const int col = j * 16 + r;
+    brow[j] = col < tl.mt ? b + (size_t)(tl.p0 + col) * row_bytes : nullptr;
+  }
+  f32x4 acc[RT][CT];
+#pragma unroll
+  for (int i = 0; i < RT; i++)
+#pragma unroll
+    for (int j = 0; j < CT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_steps = I / S::KS;
+  wave_dot_multi<MODE, RT, CT, U>(arow, brow, (w * n_steps) / 4, ((w + 1) * n_steps) / 4, g, acc);
+  store_partials<RT, CT>(acc, red);
+  __syncthreads();
+
+  float cs = 1.0f;
+  if (MODE == MOE_FP8_E4M3) cs = act_scale_from_bits(act_amax_bits) * w2_scale[tl.e];
+  for (int q = w; q < RT * CT; q += 4) {
+    const int i = q / CT, j = q % CT, col = j * 16 + r;
+    f32x4 v = sum_partials<RT, CT>(red, q);
+    if (col < tl.mt) {
+      if (MODE == MOE_FP8_E4M3) v *= cs;
+      *reinterpret_cast<f32x4*>(y + (size_t)(tl.p0 + col) * H + m0 + i * 16 + 4 * g) = v;
+    }
+  }
+}
+
+// Waves per block (all splitting K over one row group).  A block's waves
+// stream the same 16 rows at different K offsets, so the block's concurrent
+// loads fall in the same few DRAM pages.
 template <int MODE>
-constexpr int ksplit_w13() {
+constexpr int waves_w13() {
   return 4;
 }
+// The bf16 down projection (K = I, the longest rows) measured fastest with 16
+// waves over 4 steps of loads each.
 template <int MODE>
-constexpr int ksplit_w2() {
-  return 4;
+constexpr int waves_w2() {
+  return MODE == MOE_BF16 ? 16 : 4;
+}
+template <int MODE>
+constexpr int unroll_w2() {
+  return MODE == MOE_BF16 ? 4 : unroll_for<MODE>();
 }
 
 template <int MODE>
@@ -287,10 +482,10 @@ static void launch_w13_mode(long max_tiles, const char* b, const char* w13, cons
                             const int32_t* sorted_ids, const Tile* tiles, const Ctrl* ctrl, int H,
                             int I, int k, const uint32_t* act_amax_bits, void* h,
                             uint32_t* amax_h_bits, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
-  constexpr int KS = ksplit_w13<MODE>();
-  const long blocks = max_tiles * (I / (8 * (4 / KS)));
-  launch_on(w13_swiglu_skinny<MODE, KS>, dim3(blocks), dim3(256), st, e0, e1, b, w13, w13_scale,
-            sorted_ids, tiles, ctrl, H, I, k, act_amax_bits, h, amax_h_bits);
+  constexpr int NW = waves_w13<MODE>();
+  const long blocks = max_tiles * (I / 8);
+  launch_on(w13_swiglu_skinny<MODE, NW>, dim3(blocks), dim3(NW * 64), st, e0, e1, b, w13,
+            w13_scale, sorted_ids, tiles, ctrl, H, I, k, act_amax_bits, h, amax_h_bits);
 }
 
 template <int MODE>
@@ -298,10 +493,10 @@ static void launch_w2_mode(long max_tiles, const char* b, const char* w2, const 
                            const Tile* tiles, const Ctrl* ctrl, int H, int I,
                            const uint32_t* act_amax_bits, float* y, hipEvent_t e0, hipEvent_t e1,
                            hipStream_t st) {
-  constexpr int KS = ksplit_w2<MODE>();
-  const long blocks = max_tiles * (H / (16 * (4 / KS)));
-  launch_on(w2_skinny<MODE, KS>, dim3(blocks), dim3(256), st, e0, e1, b, w2, w2_scale, tiles, ctrl,
-            H, I, act_amax_bits, y);
+  constexpr int NW = waves_w2<MODE>();
+  const long blocks = max_tiles * (H / 16);
+  launch_on(w2_skinny<MODE, NW, unroll_w2<MODE>()>, dim3(blocks), dim3(NW * 64), st, e0, e1, b, w2, w2_scale, tiles,
+            ctrl, H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const float* w13_scale,

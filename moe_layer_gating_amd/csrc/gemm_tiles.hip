@@ -17,8 +17,9 @@
 // Weights are streamed from HBM straight into registers in MFMA operand
 // layout (no LDS round trip: every weight byte is used by exactly one wave),
 // through a ring of kPD stages per wave, so that enough bytes are in flight
-// per CU to cover HBM latency.  The token tile is shared by the 4 waves and
-// goes through LDS, double-buffered and prefetched one stage ahead.
+// per CU to cover HBM latency.  The token tile is shared by the 4 waves: it
+// is prefetched into registers through a ring of the same depth and written
+// to a double-buffered LDS tile one stage before use.
 //
 // LDS layout of a token stage: row r keeps its 16-byte chunk c at slot
 // c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7.  Eight consecutive rows read at
@@ -37,7 +38,7 @@ namespace moe {
 
 constexpr int kTileN = 128;  // weight rows per block tile
 constexpr int kStageB = 128;  // bytes of K per row per stage
-constexpr int kPD = 4;        // weight stages in flight per wave
+constexpr int kPD = 3;        // weight stages in flight per wave
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -79,7 +80,7 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 //   b_rows[i]: this thread's staged token rows r0 + 32 i, already offset by
 //              the thread's chunk (t & 7) * 16;
 //   acc[i][j]: row tile i, column tile j of the wave's 32 x BM accumulator.
-template <int MODE, int BM>
+template <int MODE, int BM, int PD>
 __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const char* const* b_rows,
                                               int n_stages, char* lds, f32x4 (*acc)[BM / 16]) {
   typedef TileMma<MODE> M;
@@ -103,9 +104,12 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   const int b_base = r16 * kStageB;
   const int cb0 = M::chunk(g, 0), cb1 = M::chunk(g, 1), r16h = r16 >> 3;
 
-  // The loop body has no data-dependent branches: prefetch stage indices are
-  // clamped to the last stage (an overrun re-reads it), and the stages that
-  // pad the final group of kPD use zero weight fragments.
+  // Both operands are prefetched PD stages ahead: a wave's loads complete in
+  // issue order, so waiting for a stage's token chunk also waits for every
+  // load issued before it, and a shorter token prefetch would drain the
+  // weight ring.  The loop body has no data-dependent branches: prefetch
+  // stage indices are clamped to the last stage (an overrun re-reads it), and
+  // the stages that pad the final group of PD use zero weight fragments.
   const int last = n_stages - 1;
   auto load_a = [&](int kt, i32x8* dst) {
     const size_t off = (size_t)kt * kStageB;
@@ -114,27 +118,28 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       dst[i] = join(*reinterpret_cast<const i32x4*>(a_rows[i] + off + ca0),
                     *reinterpret_cast<const i32x4*>(a_rows[i] + off + ca1));
   };
-  i32x8 ra[kPD][2];
+  auto load_b = [&](int kt, i32x4* dst) {
+    const size_t off = (size_t)kt * kStageB;
 #pragma unroll
-  for (int p = 0; p < kPD; p++) load_a(min(p, last), ra[p]);
-  i32x4 rb[NB];
+    for (int i = 0; i < NB; i++) dst[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
+  };
+  i32x8 ra[PD][2];
+  i32x4 rb[PD][NB];
 #pragma unroll
-  for (int i = 0; i < NB; i++) rb[i] = *reinterpret_cast<const i32x4*>(b_rows[i]);
-#pragma unroll
-  for (int i = 0; i < NB; i++) *reinterpret_cast<i32x4*>(lds + b_slot[i]) = rb[i];
-  {
-    const size_t off = (size_t)min(1, last) * kStageB;
-#pragma unroll
-    for (int i = 0; i < NB; i++) rb[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
+  for (int p = 0; p < PD; p++) {
+    load_a(min(p, last), ra[p]);
+    load_b(min(p, last), rb[p]);
   }
+#pragma unroll
+  for (int i = 0; i < NB; i++) *reinterpret_cast<i32x4*>(lds + b_slot[i]) = rb[0][i];
   __syncthreads();
 
   const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int n_groups = (n_stages + kPD - 1) / kPD;
+  const int n_groups = (n_stages + PD - 1) / PD;
   for (int grp = 0; grp < n_groups; grp++) {
 #pragma unroll
-    for (int q = 0; q < kPD; q++) {
-      const int kt = grp * kPD + q;
+    for (int q = 0; q < PD; q++) {
+      const int kt = grp * PD + q;
       const bool valid = kt < n_stages;
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
@@ -148,13 +153,14 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
         acc[0][j] = M::mma(a0, fb, acc[0][j]);
         acc[1][j] = M::mma(a1, fb, acc[1][j]);
       }
-      load_a(min(kt + kPD, last), ra[q]);
+      // the token chunk of stage kt+1 (ring slot (q+1) % PD) into the other
+      // LDS buffer, then refill slot q with stage kt+PD
       char* nxt = lds + ((kt + 1) & 1) * B_BYTES;
 #pragma unroll
-      for (int i = 0; i < NB; i++) *reinterpret_cast<i32x4*>(nxt + b_slot[i]) = rb[i];
-      const size_t off = (size_t)min(kt + 2, last) * kStageB;
-#pragma unroll
-      for (int i = 0; i < NB; i++) rb[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
+      for (int i = 0; i < NB; i++)
+        *reinterpret_cast<i32x4*>(nxt + b_slot[i]) = rb[(q + 1) % PD][i];
+      load_a(min(kt + PD, last), ra[q]);
+      load_b(min(kt + PD, last), rb[q]);
       __syncthreads();
     }
   }
@@ -165,8 +171,8 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
 // q = R / 16 row 2i is gate feature nb*64 + 8q + i, row 2i+1 the matching up
 // feature, so a lane's accumulator rows 4g..4g+3 hold gate/up/gate/up of
 // features nb*64 + 8q + 2g and + 1.
-template <int MODE, int BM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
+template <int MODE, int BM, int PD = kPD, int WPE = 2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void w13_swiglu_tiles(
     const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
     const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
+  tile_mainloop<MODE, BM, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
 
   float cs = 1.0f;
   if (MODE == MOE_FP8_E4M3) {
@@ -246,8 +252,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // -------------------------------------------------------------------- w2
-template <int MODE, int BM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict__ b,
+template <int MODE, int BM, int PD = kPD, int WPE = 2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void w2_tiles(const char* __restrict__ b,
                                                 const char* __restrict__ w2,
                                                 const float* __restrict__ w2_scale,
                                                 const Tile* __restrict__ tiles,
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
+  tile_mainloop<MODE, BM, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
 
   float cs = 1.0f;
   if (MODE == MOE_FP8_E4M3) {

@@ -13,6 +13,8 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kSkinnyBM = 16;  // sorted positions per tile of the few-token GEMMs
 constexpr int kRouteSmallMax = 256;  // pairs routed by the one-block front kernel
+constexpr int kSortChunk = 1024;     // pairs per chunk of the many-pair grouping (one per thread)
+constexpr int kChunkSortMin = 8192;  // pairs from which the chunked grouping is used
 constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -106,6 +108,13 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                               int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
                               const uint16_t* x, int H, uint8_t* xq, hipStream_t st);
+// Grouping of n pairs in chunks of kSortChunk plus the tile list of <= bm
+// positions (three launches).  Scratch: chunk_counts and base hold
+// ceil(n / kSortChunk) * E ints each, rank n ints.
+hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
+                             int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
+                             int32_t* rank, hipStream_t st);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
                               int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);

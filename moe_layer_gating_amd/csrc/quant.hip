@@ -24,71 +24,90 @@ __device__ __forceinline__ float amax_to_scale(uint32_t bits) {
   return a > 0.f ? a / 448.0f : 1.0f;
 }
 
-// max |src| over n bf16 values (n a multiple of 8, src 16-byte aligned).
+// max |src| over n bf16 values (n a multiple of 8, src 16-byte aligned); each
+// thread keeps four 16-byte loads in flight.
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ src, long n8,
                                                         uint32_t* amax_bits) {
   __shared__ float part[4];
   float m = 0.f;
   const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n8;
-       i += (long)gridDim.x * blockDim.x) {
-    i32x4 v = s4[i];
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i0 = blockIdx.x * (long)blockDim.x + threadIdx.x; i0 < n8; i0 += 4 * stride) {
+    i32x4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      uint32_t u = (uint32_t)v[q];
-      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(u & 0xffffu))));
-      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(u >> 16))));
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      v[u] = i < n8 ? s4[i] : i32x4{0, 0, 0, 0};
     }
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        uint32_t w = (uint32_t)v[u][q];
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(w & 0xffffu))));
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(w >> 16))));
+      }
   }
   m = wave_max(m);
   if (lane_id() == 0) part[threadIdx.x / kWave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-    atomicMax(amax_bits, __float_as_uint(b));
+    // read first: most blocks then skip the atomic on the single address
+    const uint32_t b = __float_as_uint(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
+    if (b > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, b);
   }
 }
 
 hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hipStream_t st) {
   long n8 = n / 8;
-  long blocks = (n8 + 255) / 256;
+  long blocks = (n8 + 1023) / 1024;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   amax_bf16_kernel<<<(int)blocks, 256, 0, st>>>(src, n8, amax_bits);
   return hipGetLastError();
 }
 
-// codes = e4m3(bf16 * 448/amax); 8 values per thread per step.
+__device__ __forceinline__ uint2 quant8(i32x4 v, float r) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    uint32_t u = (uint32_t)v[q], u2 = (uint32_t)v[q + 2];
+    lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u & 0xffffu)) * r) << (16 * q);
+    lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u >> 16)) * r) << (16 * q + 8);
+    hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 & 0xffffu)) * r) << (16 * q);
+    hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 >> 16)) * r) << (16 * q + 8);
+  }
+  return make_uint2(lo, hi);
+}
+
+// codes = e4m3(bf16 * 448/amax); 8 values per 16-byte load, four loads in
+// flight per thread.
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(const uint16_t* __restrict__ src, long n8,
                                                          const uint32_t* __restrict__ amax_bits,
                                                          uint8_t* __restrict__ dst) {
   const float r = amax_to_mult(*amax_bits);
   const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
   uint2* d2 = reinterpret_cast<uint2*>(dst);
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n8;
-       i += (long)gridDim.x * blockDim.x) {
-    i32x4 v = s4[i];
-    uint32_t lo = 0, hi = 0;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i0 = blockIdx.x * (long)blockDim.x + threadIdx.x; i0 < n8; i0 += 4 * stride) {
+    i32x4 v[4];
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      uint32_t u = (uint32_t)v[q];
-      lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u & 0xffffu)) * r) << (16 * q);
-      lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u >> 16)) * r) << (16 * q + 8);
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      v[u] = i < n8 ? s4[i] : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      uint32_t u = (uint32_t)v[q + 2];
-      hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u & 0xffffu)) * r) << (16 * q);
-      hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u >> 16)) * r) << (16 * q + 8);
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      if (i < n8) d2[i] = quant8(v[u], r);
     }
-    d2[i] = make_uint2(lo, hi);
   }
 }
 
 hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_bits, uint8_t* dst,
                              hipStream_t st) {
   long n8 = n / 8;
-  long blocks = (n8 + 255) / 256;
+  long blocks = (n8 + 1023) / 1024;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   quant_e4m3_kernel<<<(int)blocks, 256, 0, st>>>(src, n8, amax_bits, dst);

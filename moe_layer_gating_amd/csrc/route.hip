@@ -442,4 +442,106 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ large batches
+// Grouping of many pairs as a counting sort over chunks of kSortChunk pairs,
+// in three launches instead of one block per expert scanning every pair:
+//   chunk_rank_kernel : per chunk, the expert histogram and each pair's rank
+//                       among the earlier pairs of its chunk on the same
+//                       expert (broadcast LDS reads, no atomics decide it);
+//   chunk_scan_kernel : expert totals, offsets, and every chunk's starting
+//                       position inside each expert's group; the tile list;
+//   chunk_scatter_kernel : position = chunk base of the expert + rank.
+// Positions are therefore ordered by (expert, pair index), the same stable
+// order as the one-kernel grouping.
+__global__ __launch_bounds__(1024) void chunk_rank_kernel(const int32_t* __restrict__ ids, int n,
+                                                          int E, int32_t* __restrict__ chunk_counts,
+                                                          int32_t* __restrict__ rank) {
+  __shared__ __attribute__((aligned(16))) int s_ids[kSortChunk];
+  __shared__ int hist[1024];
+  const int t = threadIdx.x, c = blockIdx.x;
+  const int f0 = c * kSortChunk, m = min(kSortChunk, n - f0);
+  hist[t] = 0;
+  s_ids[t] = t < m ? ids[f0 + t] : -1;  // kSortChunk == blockDim.x
+  __syncthreads();
+  if (t < m) {
+    const int e = s_ids[t];
+    atomicAdd(&hist[e], 1);
+    // earlier pairs of this chunk on the same expert: 16-byte LDS reads that
+    // every lane of a wave takes from the same address (broadcast)
+    int r = 0;
+    const int4* s4 = reinterpret_cast<const int4*>(s_ids);
+    const int full = t >> 2;
+    for (int j = 0; j < full; j++) {
+      const int4 v = s4[j];
+      r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (int j = full * 4; j < t; j++) r += (s_ids[j] == e);
+    rank[f0 + t] = r;
+  }
+  __syncthreads();
+  if (t < E) chunk_counts[(size_t)c * E + t] = hist[t];
+}
+
+__global__ __launch_bounds__(1024) void chunk_scan_kernel(
+    const int32_t* __restrict__ chunk_counts, int n_chunks, int E, int n,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ base,
+    int bm, Tile* __restrict__ tiles, int32_t* num_tiles) {
+  __shared__ int tmp[16];
+  const int t = threadIdx.x;
+  int cnt = 0;
+  if (t < E)
+    for (int c = 0; c < n_chunks; c++) cnt += chunk_counts[(size_t)c * E + t];
+  const int nt = (cnt + bm - 1) / bm;
+  int total_pairs, total_tiles;
+  const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
+  const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
+  if (t < E) {
+    counts[t] = cnt;
+    offsets[t] = pre;
+    int run = pre;
+    for (int c = 0; c < n_chunks; c++) {
+      base[(size_t)c * E + t] = run;
+      run += chunk_counts[(size_t)c * E + t];
+    }
+    for (int i = 0; i < nt; i++) {
+      Tile tl;
+      tl.e = t;
+      tl.p0 = pre + i * bm;
+      tl.mt = min(bm, cnt - i * bm);
+      tl.pad = 0;
+      tiles[tpre + i] = tl;
+    }
+  }
+  if (t == 0) {
+    offsets[E] = n;
+    *num_tiles = total_tiles;
+  }
+}
+
+__global__ __launch_bounds__(1024) void chunk_scatter_kernel(const int32_t* __restrict__ ids,
+                                                             const int32_t* __restrict__ rank,
+                                                             const int32_t* __restrict__ base,
+                                                             int n, int E,
+                                                             int32_t* __restrict__ sorted_ids,
+                                                             int32_t* __restrict__ inv_perm) {
+  const int f = blockIdx.x * 1024 + threadIdx.x;
+  if (f >= n) return;
+  const int pos = base[(size_t)(f / kSortChunk) * E + ids[f]] + rank[f];
+  sorted_ids[pos] = f;
+  inv_perm[f] = pos;
+}
+
+hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
+                             int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
+                             int32_t* rank, hipStream_t st) {
+  const int n_chunks = (n + kSortChunk - 1) / kSortChunk;
+  chunk_rank_kernel<<<n_chunks, 1024, 0, st>>>(ids, n, E, chunk_counts, rank);
+  chunk_scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, n_chunks, E, n, counts, offsets, base, bm,
+                                        tiles, num_tiles);
+  chunk_scatter_kernel<<<(n + 1023) / 1024, 1024, 0, st>>>(ids, rank, base, n, E, sorted_ids,
+                                                           inv_perm);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -56,6 +56,10 @@ CASES = [
     # 16 <= mean pairs per expert < 64: 64-position tiles, some experts spill
     # into a second tile
     ("fp8_tiles64_ragged", 250, 384, 8, 2, 384, FP8, "uniform"),
+    # 8192 pairs or more: the grouping runs as a chunked counting sort (ragged
+    # last chunk) inside the fused entry point
+    ("fp8_tiles_chunked_sort", 1100, 256, 16, 8, 256, FP8, "zipf"),
+    ("bf16_tiles_chunked_sort", 4200, 128, 64, 2, 128, BF16, "uniform"),
 ]
 IDS = [c[0] for c in CASES]
 
