@@ -20,7 +20,9 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   (profiles/traffic.json), null when the kernel sources have
                   changed since those counters were taken;
   cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
-                  the same workload (whole layers, about 10 s).
+                  the same workload (whole layers, about 10 s);
+  graph_replay -- the same step replayed from a captured HIP graph, as a
+                  separate figure.
 """
 from __future__ import annotations
 
@@ -224,6 +226,22 @@ def main():
     ms = elapsed * 1e3 / args.steps
     w13_ms = float(np.mean([elapsed_ms(a, b) for a, b in pairs]))
 
+    # the same step replayed from a captured HIP graph (a separate, labelled
+    # figure: kernel launches without per-launch CPU work; `value` stays the
+    # eagerly launched rate)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph
+
     # per-stage breakdown (outside the timed region; every boundary recorded)
     evs = [new_event() for _ in range(moe.NUM_STAGE_EVENTS)]
     reps = min(args.steps, 20)
@@ -266,6 +284,8 @@ def main():
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_tf,
         "layer_alg_bytes": layer_bytes,
+        "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": spec.T / (graph_ms * 1e-3),
+                         "layer_hbm_frac": layer_bytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "stage_ms": {n: round(float(v), 5) for n, v in zip(
             ["gating", "align_sort", "tiles", "x_quant", "w13_swiglu", "h_quant", "w2",
              "combine"], stage_ms)},

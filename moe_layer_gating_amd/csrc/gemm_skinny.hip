@@ -264,201 +264,6 @@ __global__ __launch_bounds__(NW * 64) void w2_skinny(const char* __restrict__ b,
   *reinterpret_cast<f32x4*>(y + (size_t)(tl.p0 + r) * H + m0 + 4 * g) = acc;
 }
 
-// ------------------------------------------------ several tiles per block
-// The same decomposition for tiles of up to 16*CT sorted positions: a block's
-// 4 waves split K over RT*16 weight rows, and every weight fragment a lane
-// loads feeds CT MFMAs (one per 16-token column tile), every token fragment
-// RT.  The K split keeps the block's concurrent weight loads inside the same
-// few rows (DRAM pages) as in the one-tile kernels.
-template <int MODE, int RT, int CT, int U>
-__device__ __forceinline__ void wave_dot_multi(const char* const* arow, const char* const* brow,
-                                               int s0, int s1, int g, f32x4 (*acc)[CT]) {
-  typedef Step<MODE> S;
-  constexpr int STEP_BYTES = S::KS * S::ES;
-  const int lane_off = g * S::LANE_K * S::ES;
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    typename S::Frag a[U][RT], b[U][CT];
-#pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int i = 0; i < RT; i++) a[u][i] = S::load(arow[i] + (size_t)(s + u) * STEP_BYTES + lane_off);
-#pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int j = 0; j < CT; j++)
-        b[u][j] = brow[j] ? S::load(brow[j] + (size_t)(s + u) * STEP_BYTES + lane_off) : S::zero();
-#pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int i = 0; i < RT; i++)
-#pragma unroll
-        for (int j = 0; j < CT; j++) acc[i][j] = S::mma(a[u][i], b[u][j], acc[i][j]);
-  }
-  for (; s < s1; s++) {
-    typename S::Frag a[RT], b[CT];
-#pragma unroll
-    for (int i = 0; i < RT; i++) a[i] = S::load(arow[i] + (size_t)s * STEP_BYTES + lane_off);
-#pragma unroll
-    for (int j = 0; j < CT; j++)
-      b[j] = brow[j] ? S::load(brow[j] + (size_t)s * STEP_BYTES + lane_off) : S::zero();
-#pragma unroll
-    for (int i = 0; i < RT; i++)
-#pragma unroll
-      for (int j = 0; j < CT; j++) acc[i][j] = S::mma(a[i], b[j], acc[i][j]);
-  }
-}
-
-// Partials of the 4 waves: red[wave][tile][lane][4]; tile q = i*CT + j is
-// finished by wave q % 4 as ((w0 + w1) + w2) + w3.
-template <int RT, int CT>
-__device__ __forceinline__ void store_partials(f32x4 (*acc)[CT], float (*red)[RT * CT][64][4]) {
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int i = 0; i < RT; i++)
-#pragma unroll
-    for (int j = 0; j < CT; j++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) red[w][i * CT + j][lane][v] = acc[i][j][v];
-}
-
-template <int RT, int CT>
-__device__ __forceinline__ f32x4 sum_partials(float (*red)[RT * CT][64][4], int q) {
-  const int lane = lane_id();
-  f32x4 v;
-#pragma unroll
-  for (int c = 0; c < 4; c++)
-    v[c] = ((red[0][q][lane][c] + red[1][q][lane][c]) + red[2][q][lane][c]) + red[3][q][lane][c];
-  return v;
-}
-
-// w13: block = RT row groups of 8 gate + 8 up features (interleaved as in
-// w13_swiglu_skinny), n0 = first feature; token column c of a tile is its
-// sorted position p0 + c.
-template <int MODE, int RT, int CT, int U = unroll_for<MODE>()>
-__global__ __launch_bounds__(256) void w13_swiglu_wide(
-    const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
-    const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
-    void* __restrict__ h, uint32_t* amax_h_bits) {
-  typedef Step<MODE> S;
-  __shared__ float red[4][RT * CT][64][4];
-  const int blocks_per_tile = I / (8 * RT);
-  const int tile_idx = blockIdx.x / blocks_per_tile;
-  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
-  if (tile_idx >= *num_tiles) return;
-  const Tile tl = tiles[tile_idx];
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int r = lane & 15, g = lane >> 4;
-  const int n0 = rb * RT * 8;
-  const size_t row_bytes = (size_t)H * S::ES;
-  const char* arow[RT];
-#pragma unroll
-  for (int i = 0; i < RT; i++) {
-    const int f = n0 + i * 8 + (r >> 1);
-    arow[i] = w13 + ((size_t)tl.e * 2 * I + ((r & 1) ? I + f : f)) * row_bytes;
-  }
-  const char* brow[CT];
-#pragma unroll
-  for (int j = 0; j < CT; j++) {
-    const int col = j * 16 + r;
-    brow[j] = col < tl.mt ? b + (size_t)(sorted_ids[tl.p0 + col] / k) * row_bytes : nullptr;
-  }
-  f32x4 acc[RT][CT];
-#pragma unroll
-  for (int i = 0; i < RT; i++)
-#pragma unroll
-    for (int j = 0; j < CT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n_steps = H / S::KS;
-  wave_dot_multi<MODE, RT, CT, U>(arow, brow, (w * n_steps) / 4, ((w + 1) * n_steps) / 4, g, acc);
-  store_partials<RT, CT>(acc, red);
-  __syncthreads();
-
-  float cs = 1.0f;
-  if (MODE == MOE_FP8_E4M3) cs = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
-  float hmax = 0.f;
-  for (int q = w; q < RT * CT; q += 4) {
-    const int i = q / CT, j = q % CT, col = j * 16 + r;
-    const f32x4 v = sum_partials<RT, CT>(red, q);
-    if (col < tl.mt) {
-      float hv[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; e2++) {
-        float gv = v[2 * e2], uv = v[2 * e2 + 1];
-        if (MODE == MOE_FP8_E4M3) {
-          gv *= cs;
-          uv *= cs;
-        }
-        hv[e2] = gv / (1.0f + expf(-gv)) * uv;
-      }
-      const size_t o = (size_t)(tl.p0 + col) * I + n0 + i * 8 + 2 * g;
-      if (MODE == MOE_F32) {
-        *reinterpret_cast<float2*>(reinterpret_cast<float*>(h) + o) = make_float2(hv[0], hv[1]);
-      } else {
-        const uint16_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]);
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(h) + o) =
-            (uint32_t)h0 | ((uint32_t)h1 << 16);
-        hmax = fmaxf(hmax, fmaxf(fabsf(bf16_to_f32(h0)), fabsf(bf16_to_f32(h1))));
-      }
-    }
-  }
-  if (MODE == MOE_FP8_E4M3) {
-    hmax = wave_max(hmax);
-    if (lane == 0) amax_update(amax_h_bits, hmax);
-  }
-}
-
-// w2: block = RT row groups of 16 output features starting at m0.
-template <int MODE, int RT, int CT, int U = unroll_for<MODE>()>
-__global__ __launch_bounds__(256) void w2_wide(const char* __restrict__ b,
-                                               const char* __restrict__ w2,
-                                               const float* __restrict__ w2_scale,
-                                               const Tile* __restrict__ tiles,
-                                               const int32_t* __restrict__ num_tiles, int H, int I,
-                                               const uint32_t* act_amax_bits,
-                                               float* __restrict__ y) {
-  typedef Step<MODE> S;
-  __shared__ float red[4][RT * CT][64][4];
-  const int blocks_per_tile = H / (16 * RT);
-  const int tile_idx = blockIdx.x / blocks_per_tile;
-  const int rb = blockIdx.x - tile_idx * blocks_per_tile;
-  if (tile_idx >= *num_tiles) return;
-  const Tile tl = tiles[tile_idx];
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int r = lane & 15, g = lane >> 4;
-  const int m0 = rb * RT * 16;
-  const size_t row_bytes = (size_t)I * S::ES;
-  const char* arow[RT];
-#pragma unroll
-  for (int i = 0; i < RT; i++) arow[i] = w2 + ((size_t)tl.e * H + m0 + i * 16 + r) * row_bytes;
-  const char* brow[CT];
-#pragma unroll
-  for (int j = 0; j < CT; j++) {
-    const int col = j * 16 + r;
-    brow[j] = col < tl.mt ? b + (size_t)(tl.p0 + col) * row_bytes : nullptr;
-  }
-  f32x4 acc[RT][CT];
-#pragma unroll
-  for (int i = 0; i < RT; i++)
-#pragma unroll
-    for (int j = 0; j < CT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n_steps = I / S::KS;
-  wave_dot_multi<MODE, RT, CT, U>(arow, brow, (w * n_steps) / 4, ((w + 1) * n_steps) / 4, g, acc);
-  store_partials<RT, CT>(acc, red);
-  __syncthreads();
-
-  float cs = 1.0f;
-  if (MODE == MOE_FP8_E4M3) cs = act_scale_from_bits(act_amax_bits) * w2_scale[tl.e];
-  for (int q = w; q < RT * CT; q += 4) {
-    const int i = q / CT, j = q % CT, col = j * 16 + r;
-    f32x4 v = sum_partials<RT, CT>(red, q);
-    if (col < tl.mt) {
-      if (MODE == MOE_FP8_E4M3) v *= cs;
-      *reinterpret_cast<f32x4*>(y + (size_t)(tl.p0 + col) * H + m0 + i * 16 + 4 * g) = v;
-    }
-  }
-}
-
 // Waves per block (all splitting K over one row group).  A block's waves
 // stream the same 16 rows at different K offsets, so the block's concurrent
 // loads fall in the same few DRAM pages.
