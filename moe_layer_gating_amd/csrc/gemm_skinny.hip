@@ -74,6 +74,30 @@ struct Step<MOE_FP8_E4M3> {
   }
 };
 
+// FP8 codes on the bf16 MFMA (kFp8ViaBf16): the same 32 codes per lane as
+// Step<MOE_FP8_E4M3>, widened to bf16; the u-th of four
+// v_mfma_f32_16x16x32_bf16 takes the lane's codes 8u .. 8u+7 of A and of B,
+// so a step sums the same 128 products.
+template <>
+struct Step<kFp8ViaBf16> {
+  static constexpr int KS = 128;
+  static constexpr int LANE_K = 32;
+  static constexpr int ES = 1;
+  typedef i32x8 Frag;
+  static __device__ __forceinline__ Frag load(const char* p) {
+    return Step<MOE_FP8_E4M3>::load(p);
+  }
+  static __device__ __forceinline__ Frag zero() { return Step<MOE_FP8_E4M3>::zero(); }
+  static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a[2 * u], a[2 * u + 1])),
+          __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(b[2 * u], b[2 * u + 1])), c, 0, 0, 0);
+    return c;
+  }
+};
+
 // fp32: four v_mfma_f32_16x16x4_f32 per step; 4 floats (16 B) per lane,
 // the i-th MFMA of the step uses the lane's i-th float.
 template <>
@@ -100,7 +124,7 @@ struct Step<MOE_F32> {
 // decode shapes).
 template <int MODE>
 constexpr int unroll_for() {
-  return MODE == MOE_FP8_E4M3 ? 4 : 8;
+  return is_fp8(MODE) ? 4 : 8;
 }
 
 // Partial product of one wave: A row `arow` (this lane's weight row), B row
@@ -202,14 +226,14 @@ __global__ __launch_bounds__(NW * 64) void w13_swiglu_skinny(
   if (w != 0) return;
 
   float c = 1.0f;
-  if (MODE == MOE_FP8_E4M3) c = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
+  if (is_fp8(MODE)) c = act_scale_from_bits(act_amax_bits) * w13_scale[tl.e];
   float hmax = 0.f;
   if (r < tl.mt) {
     float hv[2];
 #pragma unroll
     for (int q = 0; q < 2; q++) {
       float gv = acc[2 * q], uv = acc[2 * q + 1];
-      if (MODE == MOE_FP8_E4M3) {
+      if (is_fp8(MODE)) {
         gv *= c;
         uv *= c;
       }
@@ -225,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void w13_swiglu_skinny(
       hmax = fmaxf(fabsf(bf16_to_f32(h0)), fabsf(bf16_to_f32(h1)));
     }
   }
-  if (MODE == MOE_FP8_E4M3) {
+  if (is_fp8(MODE)) {
     hmax = wave_max(hmax);
     if (lane == 0) amax_update(amax_h_bits, hmax);
   }
@@ -319,8 +343,8 @@ hipError_t launch_w13_swiglu(int mode, const void* b, const void* w13, const flo
     launch_w13_mode<MOE_BF16>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
                               act_amax_bits, h, amax_h_bits, e0, e1, st);
   else
-    launch_w13_mode<MOE_FP8_E4M3>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
-                                  act_amax_bits, h, amax_h_bits, e0, e1, st);
+    launch_w13_mode<kFp8ViaBf16>(max_tiles, bb, ww, w13_scale, sorted_ids, tiles, ctrl, H, I, k,
+                                 act_amax_bits, h, amax_h_bits, e0, e1, st);
   return hipGetLastError();
 }
 

@@ -3,10 +3,12 @@
 //
 // When an expert receives tens to thousands of tokens, its weight rows are
 // used against many tokens and the GEMM becomes a 2-D tiled contraction.  A
-// block owns a 128 (weight rows) x BM (sorted positions of one expert) output
-// tile and walks the reduction dimension K in 128-byte stages (128 FP8 codes
-// or 64 bf16 values per row).  Each of its 4 waves owns 32 weight rows (two
-// 16-row MFMA tiles) and all BM columns.
+// block owns a 128*WN (weight rows) x BM (sorted positions of one expert)
+// output tile and walks the reduction dimension K in 128-byte stages (128 FP8
+// codes or 64 bf16 values per row).  Each of its 4*WN waves owns 32 weight
+// rows (two 16-row MFMA tiles) and all BM columns.  With WN = 2 each staged
+// token tile serves 256 weight rows, which halves the token-side L2 requests
+// per weight byte (both operands' requests share the CU's path to L2).
 //
 // The expert rows sit on the MFMA row side and the tokens on the column side,
 // as in the decode kernels (codebridge-ai.com, "aws-moe-kernel-wgmma-triton-
@@ -27,8 +29,20 @@
 // rows counted over two 128-byte bank rows, so neither the stores nor the
 // MFMA fragment reads conflict in the LDS banks.
 //
+// FP8 gate/up projection (kFp8ViaBf16): the token stage is widened to bf16
+// as it is written to LDS and the weight fragments are widened in registers;
+// the products then go through the bf16 MFMA, whose sums are exact where the
+// FP8 MFMA's are not.  A widened row is 256 bytes (16 chunks, chunk q holding
+// K values 8q .. 8q+7) and keeps chunk q at slot rot(q) ^ vswz(r), with
+// rot(q) = (q >> 1) | ((q & 1) << 3) and, for m = r & 15, vswz(r) = swz(m) |
+// (((m ^ (m >> 1)) & 1) << 3).  The 8 lanes staging one row store chunks 2c (then 2c+1), which
+// rot spreads over all 8 slots of a 128-byte bank row; a plain XOR layout
+// leaves them on 4 and the counters showed every access of the kernel
+// taking twice as long.  The fragment reads of 8, 16 and 32 consecutive
+// lanes, and the stores, hit distinct 16-byte bank groups.
+//
 // Launch order: block b takes tile b / NB and weight-row block b % NB, with
-// NB = (rows of the weight matrix) / 128.  Blocks are dealt to the 8 XCDs
+// NB = (rows of the weight matrix) / (128*WN).  Blocks are dealt to the 8 XCDs
 // round-robin, so when NB is a multiple of 8 a given weight-row block of an
 // expert always runs on the same XCD and its reuse across the expert's
 // token tiles can be served by that XCD's L2.
@@ -36,11 +50,17 @@
 
 namespace moe {
 
-constexpr int kTileN = 128;  // weight rows per block tile
+constexpr int kTileN = 128;  // weight rows per 4 waves
 constexpr int kStageB = 128;  // bytes of K per row per stage
 constexpr int kPD = 3;        // weight stages in flight per wave
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// a function of r & 15, so a fragment read may pass its row within the tile
+__device__ __forceinline__ int vswz(int r) {
+  r &= 15;
+  return ((r ^ (r >> 3)) & 7) | (((r ^ (r >> 1)) & 1) << 3);
+}
+__device__ __forceinline__ int vrot(int q) { return (q >> 1) | ((q & 1) << 3); }
 
 // One 128-byte K stage of a 16x16 output tile: each lane supplies 32 bytes
 // of its row of each operand, as two 16-byte chunks (h = 0, 1).
@@ -77,15 +97,27 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 
 // Main loop shared by both projections.
 //   a_rows[i]: this lane's weight row of the wave's row tile i (K offset 0);
-//   b_rows[i]: this thread's staged token rows r0 + 32 i, already offset by
-//              the thread's chunk (t & 7) * 16;
+//   b_rows[i]: this thread's staged token rows r0 + 32*WN*i, already offset
+//              by the thread's chunk (t & 7) * 16;
+//   live:      column tiles holding positions of the tile, ceil(mt / 16); the
+//              MFMAs and LDS reads of the others (all padding) are skipped
+//              by a wave-uniform branch;
 //   acc[i][j]: row tile i, column tile j of the wave's 32 x BM accumulator.
-template <int MODE, int BM, int PD>
+// LDS bytes of one token-stage buffer.
+template <int MODE, int BM>
+constexpr int stage_lds_bytes() {
+  return BM * kStageB * (MODE == kFp8ViaBf16 ? 2 : 1);
+}
+
+template <int MODE, int BM, int WN, int PD>
 __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const char* const* b_rows,
-                                              int n_stages, char* lds, f32x4 (*acc)[BM / 16]) {
-  typedef TileMma<MODE> M;
-  constexpr int B_BYTES = BM * kStageB;  // one LDS buffer
-  constexpr int NB = BM / 32;            // token rows staged per thread
+                                              int n_stages, int live, char* lds,
+                                              f32x4 (*acc)[BM / 16]) {
+  constexpr bool VIA = MODE == kFp8ViaBf16;
+  typedef TileMma<VIA ? MOE_FP8_E4M3 : MODE> M;
+  constexpr int ROWB = VIA ? 2 * kStageB : kStageB;  // LDS bytes per token row
+  constexpr int B_BYTES = stage_lds_bytes<MODE, BM>();
+  constexpr int NB = BM / (32 * WN);     // token rows staged per thread
   constexpr int MT = BM / 16;            // column tiles
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -93,15 +125,32 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   const int c = t & 7, r0 = t >> 3;
   const int ca0 = M::chunk(g, 0) * 16, ca1 = M::chunk(g, 1) * 16;
 
-  int b_slot[NB];
+  int b_slot[NB], b_slot2[NB];
 #pragma unroll
   for (int i = 0; i < NB; i++) {
-    const int r = r0 + 32 * i;
-    b_slot[i] = r * kStageB + ((c ^ swz(r)) << 4);
+    const int r = r0 + 32 * WN * i;
+    if (VIA) {  // bf16 chunks 2c and 2c+1 of the widened row
+      b_slot[i] = r * ROWB + ((vrot(2 * c) ^ vswz(r)) << 4);
+      b_slot2[i] = r * ROWB + ((vrot(2 * c + 1) ^ vswz(r)) << 4);
+    } else {
+      b_slot[i] = r * ROWB + ((c ^ swz(r)) << 4);
+      b_slot2[i] = 0;
+    }
   }
+  auto stage_b = [&](char* buf, const i32x4* src) {
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      if (VIA) {
+        *reinterpret_cast<i32x4*>(buf + b_slot[i]) = e4m3x8_to_bf16x8(src[i][0], src[i][1]);
+        *reinterpret_cast<i32x4*>(buf + b_slot2[i]) = e4m3x8_to_bf16x8(src[i][2], src[i][3]);
+      } else {
+        *reinterpret_cast<i32x4*>(buf + b_slot[i]) = src[i];
+      }
+    }
+  };
   // LDS offsets of this lane's two chunks in column tile j: row j*16 + r16,
   // whose swizzle is (r16 ^ (2j + r16 / 8)) & 7.
-  const int b_base = r16 * kStageB;
+  const int b_base = r16 * ROWB;
   const int cb0 = M::chunk(g, 0), cb1 = M::chunk(g, 1), r16h = r16 >> 3;
 
   // Both operands are prefetched PD stages ahead: a wave's loads complete in
@@ -130,8 +179,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
     load_a(min(p, last), ra[p]);
     load_b(min(p, last), rb[p]);
   }
-#pragma unroll
-  for (int i = 0; i < NB; i++) *reinterpret_cast<i32x4*>(lds + b_slot[i]) = rb[0][i];
+  stage_b(lds, rb[0]);
   __syncthreads();
 
   const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -144,21 +192,40 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
       const char* cur = lds + (kt & 1) * B_BYTES;
+      if (VIA) {
+        // MFMA u: the lane's codes 8u .. 8u+7 of its 32 (K values
+        // 32g + 8u ..), i.e. bf16 chunk 4g + u of the token row
 #pragma unroll
-      for (int j = 0; j < MT; j++) {
-        const int sw = (r16 ^ (2 * j + r16h)) & 7;
-        const char* rowp = cur + j * 16 * kStageB + b_base;
-        const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
-                              *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
-        acc[0][j] = M::mma(a0, fb, acc[0][j]);
-        acc[1][j] = M::mma(a1, fb, acc[1][j]);
+        for (int u = 0; u < 4; u++) {
+          const bf16x8 a0u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a0[2 * u], a0[2 * u + 1]));
+          const bf16x8 a1u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a1[2 * u], a1[2 * u + 1]));
+          const int off = b_base + ((vrot(4 * g + u) ^ vswz(r16)) << 4);
+#pragma unroll
+          for (int j = 0; j < MT; j++) {
+            if (j < live) {
+              const bf16x8 fb = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const i32x4*>(cur + j * 16 * ROWB + off));
+              acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0u, fb, acc[0][j], 0, 0, 0);
+              acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1u, fb, acc[1][j], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < MT; j++) {
+          if (j < live) {
+            const int sw = (r16 ^ (2 * j + r16h)) & 7;
+            const char* rowp = cur + j * 16 * kStageB + b_base;
+            const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
+                                  *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
+            acc[0][j] = M::mma(a0, fb, acc[0][j]);
+            acc[1][j] = M::mma(a1, fb, acc[1][j]);
+          }
+        }
       }
       // the token chunk of stage kt+1 (ring slot (q+1) % PD) into the other
       // LDS buffer, then refill slot q with stage kt+PD
-      char* nxt = lds + ((kt + 1) & 1) * B_BYTES;
-#pragma unroll
-      for (int i = 0; i < NB; i++)
-        *reinterpret_cast<i32x4*>(nxt + b_slot[i]) = rb[(q + 1) % PD][i];
+      stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % PD]);
       load_a(min(kt + PD, last), ra[q]);
       load_b(min(kt + PD, last), rb[q]);
       __syncthreads();
@@ -168,19 +235,19 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
 
 // ------------------------------------------------------------------- w13
 // Block row R (wave R / 32, row tile (R / 16) % 2, MFMA row R % 16): tile
-// q = R / 16 row 2i is gate feature nb*64 + 8q + i, row 2i+1 the matching up
-// feature, so a lane's accumulator rows 4g..4g+3 hold gate/up/gate/up of
-// features nb*64 + 8q + 2g and + 1.
-template <int MODE, int BM, int PD = kPD, int WPE = 2>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void w13_swiglu_tiles(
+// q = R / 16 row 2i is gate feature F + 8q + i (F = nb*64*WN), row 2i+1 the
+// matching up feature, so a lane's accumulator rows 4g..4g+3 hold
+// gate/up/gate/up of features F + 8q + 2g and + 1.
+template <int MODE, int BM, int WN, int PD = kPD>
+__global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
     const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
     const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
     void* __restrict__ h, uint32_t* amax_h_bits) {
-  constexpr int ES = MODE == MOE_FP8_E4M3 ? 1 : 2;
+  constexpr int ES = MODE == MOE_BF16 ? 2 : 1;
   constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB];
-  const int NBLK = 2 * I / kTileN;
+  __shared__ __attribute__((aligned(16))) char lds[2 * stage_lds_bytes<MODE, BM>()];
+  const int NBLK = 2 * I / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;
   if (tile_idx >= *num_tiles) return;
@@ -194,14 +261,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int q = 2 * w + i;
-    const int f = nb * 64 + q * 8 + (r16 >> 1);
+    const int f = nb * 64 * WN + q * 8 + (r16 >> 1);
     const int wrow = (r16 & 1) ? I + f : f;
     a_rows[i] = w13 + ((size_t)tl.e * 2 * I + wrow) * row_bytes;
   }
-  const char* b_rows[BM / 32];
+  const char* b_rows[BM / (32 * WN)];
 #pragma unroll
-  for (int i = 0; i < BM / 32; i++) {
-    const int j = min(r0 + 32 * i, tl.mt - 1);
+  for (int i = 0; i < BM / (32 * WN); i++) {
+    const int j = min(r0 + 32 * WN * i, tl.mt - 1);
     const int tok = sorted_ids[tl.p0 + j] / k;
     b_rows[i] = b + (size_t)tok * row_bytes + c * 16;
   }
@@ -210,10 +277,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
+  tile_mainloop<MODE, BM, WN, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), (tl.mt + 15) >> 4,
+                                  lds, acc);
 
   float cs = 1.0f;
-  if (MODE == MOE_FP8_E4M3) {
+  if (is_fp8(MODE)) {
     const float a = __uint_as_float(*act_amax_bits);
     cs = (a > 0.f ? a / 448.0f : 1.0f) * w13_scale[tl.e];
   }
@@ -225,12 +293,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       uint16_t* hrow = reinterpret_cast<uint16_t*>(h) + (size_t)(tl.p0 + col) * I;
 #pragma unroll
       for (int i = 0; i < 2; i++) {
-        const int f = nb * 64 + (2 * w + i) * 8 + 2 * g;
+        const int f = nb * 64 * WN + (2 * w + i) * 8 + 2 * g;
         float hv[2];
 #pragma unroll
         for (int q = 0; q < 2; q++) {
           float gv = acc[i][j][2 * q], uv = acc[i][j][2 * q + 1];
-          if (MODE == MOE_FP8_E4M3) {
+          if (is_fp8(MODE)) {
             gv *= cs;
             uv *= cs;
           }
@@ -242,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       }
     }
   }
-  if (MODE == MOE_FP8_E4M3) {
+  if (is_fp8(MODE)) {
     hmax = wave_max(hmax);
     if (lane == 0) {
       const uint32_t bits = __float_as_uint(hmax);
@@ -252,8 +320,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 }
 
 // -------------------------------------------------------------------- w2
-template <int MODE, int BM, int PD = kPD, int WPE = 2>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void w2_tiles(const char* __restrict__ b,
+template <int MODE, int BM, int WN, int PD = kPD>
+__global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict__ b,
                                                 const char* __restrict__ w2,
                                                 const float* __restrict__ w2_scale,
                                                 const Tile* __restrict__ tiles,
@@ -263,7 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   constexpr int ES = MODE == MOE_FP8_E4M3 ? 1 : 2;
   constexpr int MT = BM / 16;
   __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB];
-  const int NBLK = H / kTileN;
+  const int NBLK = H / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;
   if (tile_idx >= *num_tiles) return;
@@ -276,11 +344,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const char* a_rows[2];
 #pragma unroll
   for (int i = 0; i < 2; i++)
-    a_rows[i] = w2 + ((size_t)tl.e * H + nb * kTileN + w * 32 + i * 16 + r16) * row_bytes;
-  const char* b_rows[BM / 32];
+    a_rows[i] = w2 + ((size_t)tl.e * H + nb * kTileN * WN + w * 32 + i * 16 + r16) * row_bytes;
+  const char* b_rows[BM / (32 * WN)];
 #pragma unroll
-  for (int i = 0; i < BM / 32; i++) {
-    const int j = min(r0 + 32 * i, tl.mt - 1);
+  for (int i = 0; i < BM / (32 * WN); i++) {
+    const int j = min(r0 + 32 * WN * i, tl.mt - 1);
     b_rows[i] = b + (size_t)(tl.p0 + j) * row_bytes + c * 16;
   }
   f32x4 acc[2][MT];
@@ -288,7 +356,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
+  tile_mainloop<MODE, BM, WN, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), (tl.mt + 15) >> 4,
+                                  lds, acc);
 
   float cs = 1.0f;
   if (MODE == MOE_FP8_E4M3) {
@@ -299,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   for (int j = 0; j < MT; j++) {
     const int col = j * 16 + r16;
     if (col < tl.mt) {
-      float* yrow = y + (size_t)(tl.p0 + col) * H + nb * kTileN + w * 32;
+      float* yrow = y + (size_t)(tl.p0 + col) * H + nb * kTileN * WN + w * 32;
 #pragma unroll
       for (int i = 0; i < 2; i++) {
         f32x4 v = acc[i][j];
@@ -310,15 +379,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
 }
 
+// 8-wave blocks (256 weight rows) for 128-position tiles when the row count
+// allows, else 4-wave blocks.  Measured: 4% faster down projection on the
+// prefill layer with 8 waves; with 64-position tiles 4 waves were faster.
+inline int tiles_wn(int bm, long rows) {
+  return (bm == 128 && rows % (2 * kTileN) == 0) ? 2 : 1;
+}
+
 template <int MODE, int BM>
 static void launch_tiles_w13_mode(long max_tiles, const char* b, const char* w13,
                                   const float* w13_scale, const int32_t* sorted_ids,
                                   const Tile* tiles, const int32_t* num_tiles, int H, int I, int k,
                                   const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
                                   hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
-  const long blocks = max_tiles * (2L * I / kTileN);
-  launch_on(w13_swiglu_tiles<MODE, BM>, dim3(blocks), dim3(256), st, e0, e1, b, w13, w13_scale,
-            sorted_ids, tiles, num_tiles, H, I, k, act_amax_bits, h, amax_h_bits);
+  if (tiles_wn(BM, 2L * I) == 2)
+    launch_on(w13_swiglu_tiles<MODE, BM, 2>, dim3(max_tiles * (2L * I / (2 * kTileN))),
+              dim3(512), st, e0, e1, b, w13, w13_scale, sorted_ids, tiles, num_tiles, H, I, k,
+              act_amax_bits, h, amax_h_bits);
+  else
+    launch_on(w13_swiglu_tiles<MODE, BM, 1>, dim3(max_tiles * (2L * I / kTileN)), dim3(256), st,
+              e0, e1, b, w13, w13_scale, sorted_ids, tiles, num_tiles, H, I, k, act_amax_bits, h,
+              amax_h_bits);
 }
 
 template <int MODE, int BM>
@@ -327,9 +408,12 @@ static void launch_tiles_w2_mode(long max_tiles, const char* b, const char* w2,
                                  const int32_t* num_tiles, int H, int I,
                                  const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
                                  hipEvent_t e1, hipStream_t st) {
-  const long blocks = max_tiles * (long)(H / kTileN);
-  launch_on(w2_tiles<MODE, BM>, dim3(blocks), dim3(256), st, e0, e1, b, w2, w2_scale, tiles,
-            num_tiles, H, I, act_amax_bits, y);
+  if (tiles_wn(BM, H) == 2)
+    launch_on(w2_tiles<MODE, BM, 2>, dim3(max_tiles * (long)(H / (2 * kTileN))), dim3(512), st,
+              e0, e1, b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
+  else
+    launch_on(w2_tiles<MODE, BM, 1>, dim3(max_tiles * (long)(H / kTileN)), dim3(256), st, e0, e1,
+              b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
@@ -348,9 +432,9 @@ hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
   else if (mode == MOE_BF16 && bm == 128)
     MOE_W13_TILES(MOE_BF16, 128);
   else if (mode == MOE_FP8_E4M3 && bm == 64)
-    MOE_W13_TILES(MOE_FP8_E4M3, 64);
+    MOE_W13_TILES(kFp8ViaBf16, 64);
   else if (mode == MOE_FP8_E4M3 && bm == 128)
-    MOE_W13_TILES(MOE_FP8_E4M3, 128);
+    MOE_W13_TILES(kFp8ViaBf16, 128);
   else
     return hipErrorInvalidValue;
 #undef MOE_W13_TILES

@@ -22,6 +22,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Internal kernel operand mode: FP8 e4m3 codes widened to bf16 in registers
+// and multiplied on the bf16 MFMA.  Every e4m3 value is exact in bf16 and the
+// bf16 MFMA sums these products in fp32 (bit-equal to the rounded exact sum
+// 99% of the time, measured); the FP8 MFMA keeps fewer bits (about 2^-19 of
+// sum|p| per instruction, measured), and its error flips rounding decisions
+// made on the result.  Used for the gate/up projection, whose output is
+// rounded to bf16 and then quantised.
+constexpr int kFp8ViaBf16 = 3;
+__host__ __device__ constexpr bool is_fp8(int mode) {
+  return mode == MOE_FP8_E4M3 || mode == kFp8ViaBf16;
+}
+
+// Eight e4m3 codes (little-endian in lo, hi) as eight bf16 values, exactly.
+__device__ __forceinline__ i32x4 e4m3x8_to_bf16x8(int lo, int hi) {
+  return i32x4{__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
 // One unit of grouped-GEMM work: `mt` consecutive sorted positions starting
 // at `p0`, all routed to expert `e`.
 struct Tile {

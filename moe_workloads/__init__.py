@@ -162,6 +162,27 @@ def make_layer(spec: LayerSpec, with_weights: bool = True):
     return layer
 
 
+def planted_logits(T, E, k, counts, seed=0):
+    """Router logits whose top-k choice hands expert e exactly counts[e] of
+    the T*k pairs (sum(counts) == T*k, every count <= T).
+
+    The pairs are listed expert by expert and pair i goes to token i % T, so
+    a token's k experts are distinct (an expert's run of <= T pairs never
+    wraps onto the same token twice).  A token's j-th planted expert gets a
+    logit near 8 - 2j; every other logit is drawn from N(0, 0.5^2) clipped
+    below 2, so the planted experts are the top k in their planted order.
+    """
+    counts = np.asarray(counts, np.int64)
+    assert counts.size == E and counts.sum() == T * k and counts.max(initial=0) <= T
+    g = np.random.default_rng(seed)
+    logits = np.minimum(g.normal(0.0, 0.5, (T, E)), 2.0)
+    experts = np.repeat(np.arange(E), counts)
+    for i, e in enumerate(experts):
+        t, j = i % T, i // T
+        logits[t, e] = 8.0 - 2.0 * j + 0.1 * g.random()
+    return np.ascontiguousarray(logits.astype(np.float32))
+
+
 def scaled(name, T, H, E, k, I, mode, routing="uniform", seed=0):
     """A layer of arbitrary shape drawn with the same recipe."""
     return LayerSpec(name, T, H, E, k, I, mode, routing=routing, seed=seed)

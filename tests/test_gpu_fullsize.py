@@ -155,7 +155,7 @@ def test_prefill_fp8_full_sampled():
     ratio = bf16_step_ratio(hv[pos], oracle.to_f64(href, FP8))
     say("  sampled h: step ratio %.3f, identical %.4f" % (ratio, np.mean(hg[pos] == href)))
     assert ratio <= 1.0
-    assert np.mean(hg[pos] == href) > 0.95
+    assert np.mean(hg[pos] == href) > 0.99
 
 
 def test_prefill_shaped_slice_full():

@@ -11,10 +11,11 @@ per-mode tolerance on max|gpu - ref| / max|ref| (fp32 1e-5, bf16 5e-3, FP8
 output type (both sides rounding to bf16 could otherwise differ by one
 output ulp, up to 2^-7 of max|ref|, for results that are both correct).
 Stage bars are tighter: h within one bf16 step of the oracle (see
-gpu_helpers.bf16_step_ratio); y (fp32) within 1e-5, except FP8 where the
-gfx950 FP8 MFMA's own accumulation error (median ~3e-5 relative per dot
-product, measured) sets the bar at 2e-4 and the share of bit-identical bf16 h
-values at 95%.
+gpu_helpers.bf16_step_ratio) and at least 99% of its bf16 values identical
+(the FP8 gate/up products go through the bf16 MFMA on widened codes, which
+sums them exactly); y (fp32) within 1e-5, except FP8 where the down
+projection's FP8 MFMA rounds its sums (about 2^-19 of sum|p| per
+instruction, measured) and the bar is 2e-4.
 Each stage is fed the oracle's upstream outputs so a failure names its stage.
 """
 import numpy as np
@@ -124,7 +125,7 @@ def test_w13_swiglu(c):
         # every element within one bf16 step of the oracle's (see
         # bf16_step_ratio), almost all equal
         assert bf16_step_ratio(hv, rv) <= 1.0
-        assert np.mean(hg == ref["h"]) > (0.95 if mode == FP8 else 0.99)
+        assert np.mean(hg == ref["h"]) > 0.99
     if mode == FP8:
         s = sc.cpu().numpy()
         _, s_x, _ = oracle.act_quant(L["x"], BF16)
@@ -254,3 +255,55 @@ def test_align_sort_large_skewed():
     assert np.array_equal(offsets.cpu().numpy(), ro)
     assert np.array_equal(sorted_ids.cpu().numpy(), rs)
     assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+# Planted routing: expert counts on both sides of the 64- and 128-position
+# tile boundaries (0, 1, 63, 64, 127, 128, 129, 256, 640, ...), so experts
+# get exact, ragged and single-row last tiles.  The last layer has 8400
+# pairs: grouping by the chunked counting sort.
+PLANTED = [
+    # name, T, H, E, k, I, mode, counts
+    ("fp8_planted_tile_edges", 1436, 256, 8, 1, 256, FP8, [0, 1, 127, 128, 129, 255, 256, 540]),
+    ("bf16_planted_tile_edges", 1436, 384, 8, 1, 128, BF16, [540, 256, 255, 129, 128, 127, 1, 0]),
+    ("fp8_planted_tiles64", 700, 256, 16, 1, 256, FP8,
+     [0, 1, 15, 16, 17, 63, 64, 65, 100, 127, 128, 33, 32, 31, 8, 0]),
+    ("fp8_planted_chunked", 4200, 256, 8, 2, 128, FP8, [0, 256, 257, 511, 1024, 1280, 2520, 2552]),
+]
+
+
+@pytest.mark.parametrize("c", PLANTED, ids=[c[0] for c in PLANTED])
+def test_planted_tile_edges(c):
+    name, T, H, E, k, I, mode, counts = c
+    L = wl.make_layer(wl.scaled(name, T, H, E, k, I, mode, seed=len(name)))
+    L["logits"] = wl.planted_logits(T, E, k, counts, seed=len(name))
+    ref = oracle.forward(mode, L["x"], L["logits"], L["w13"], L["w13_scale"], L["w2"],
+                         L["w2_scale"], k)
+    assert np.array_equal(ref["counts"], np.array(counts, np.int32))
+    D = upload(L)
+    say("planted fused", name)
+    out = moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
+                                D["w2_scale"], k)
+    torch.cuda.synchronize()
+    og = oracle.to_f64(act_to_numpy(out, mode), mode)
+    assert not np.isnan(og).any()
+    err = rel_inf(og, ref["out_exact"])
+    say("  rel err", err)
+    assert err <= OUT_TOL[mode]
+    say("planted steps", name)
+    h, sc = moe.moe_grouped_gemm_w13_swiglu(D["x"], D["w13"], D["w13_scale"],
+                                            int_tensor(ref["sorted_ids"]), int_tensor(ref["offsets"]),
+                                            k)
+    torch.cuda.synchronize()
+    hg = act_to_numpy(h, mode)
+    assert bf16_step_ratio(oracle.to_f64(hg, mode), oracle.to_f64(ref["h"], mode)) <= 1.0
+    assert np.mean(hg == ref["h"]) > 0.99
+    act = np.zeros(4, np.float32)
+    if mode == FP8:
+        _, s_h, _ = oracle.act_quant(ref["h"], BF16)
+        act[1] = s_h
+        act[3] = np.float32(np.max(np.abs(oracle.to_f64(ref["h"], BF16))))
+    y = moe.moe_grouped_gemm_w2(act_to_torch(ref["h"], mode), D["w2"], D["w2_scale"],
+                                int_tensor(ref["offsets"]), f32_tensor(act), k)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.w2(mode, ref["h"], L["w2"], L["w2_scale"], ref["offsets"], k)
+    assert rel_inf(y.cpu().numpy(), y_ref) <= (2e-4 if mode == FP8 else 1e-5)

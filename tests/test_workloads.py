@@ -56,3 +56,13 @@ def test_routing_recipes():
     # the bias is -1.1 ln(r) for a permutation r of 1..E
     ranks = np.exp(-bias / 1.1)
     assert np.allclose(np.sort(ranks), np.arange(1, 41), atol=1e-3)
+
+
+def test_planted_logits_give_the_planted_counts():
+    import oracle
+    for T, E, k, counts in ((2432, 8, 1, [0, 1, 255, 256, 257, 511, 512, 640]),
+                            (4200, 8, 2, [0, 256, 257, 511, 1024, 1280, 2520, 2552]),
+                            (5, 4, 4, [5, 5, 5, 5])):
+        ids, _ = oracle.topk_gating(wl.planted_logits(T, E, k, counts, seed=3), k)
+        assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
+        assert all(len(set(r)) == k for r in ids.tolist())
