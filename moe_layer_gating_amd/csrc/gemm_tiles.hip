@@ -99,9 +99,6 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 //   a_rows[i]: this lane's weight row of the wave's row tile i (K offset 0);
 //   b_rows[i]: this thread's staged token rows r0 + 32*WN*i, already offset
 //              by the thread's chunk (t & 7) * 16;
-//   live:      column tiles holding positions of the tile, ceil(mt / 16); the
-//              MFMAs and LDS reads of the others (all padding) are skipped
-//              by a wave-uniform branch;
 //   acc[i][j]: row tile i, column tile j of the wave's 32 x BM accumulator.
 // LDS bytes of one token-stage buffer.
 template <int MODE, int BM>
@@ -109,10 +106,10 @@ constexpr int stage_lds_bytes() {
   return BM * kStageB * (MODE == kFp8ViaBf16 ? 2 : 1);
 }
 
-template <int MODE, int BM, int WN, int PD>
+template <int MODE, int BM, int WN, int PD, int MTA>
 __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const char* const* b_rows,
-                                              int n_stages, int live, char* lds,
-                                              f32x4 (*acc)[BM / 16]) {
+                                              int n_stages, char* lds, f32x4 (*acc)[MTA]) {
+  static_assert(BM / 16 <= MTA && BM % (32 * WN) == 0, "tile shape");
   constexpr bool VIA = MODE == kFp8ViaBf16;
   typedef TileMma<VIA ? MOE_FP8_E4M3 : MODE> M;
   constexpr int ROWB = VIA ? 2 * kStageB : kStageB;  // LDS bytes per token row
@@ -156,9 +153,12 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   // Both operands are prefetched PD stages ahead: a wave's loads complete in
   // issue order, so waiting for a stage's token chunk also waits for every
   // load issued before it, and a shorter token prefetch would drain the
-  // weight ring.  The loop body has no data-dependent branches: prefetch
-  // stage indices are clamped to the last stage (an overrun re-reads it), and
-  // the stages that pad the final group of PD use zero weight fragments.
+  // weight ring.  The ring has PD + 1 register slots, so the loads of stage
+  // kt+PD go into the slot stage kt-1 has freed and are issued before the
+  // MFMAs of stage kt, which then run while PD stages are in flight.  The
+  // loop body has no data-dependent branches: prefetch stage indices are
+  // clamped to the last stage (an overrun re-reads it), and the stages that
+  // pad the final group of PD + 1 use zero weight fragments.
   const int last = n_stages - 1;
   auto load_a = [&](int kt, i32x8* dst) {
     const size_t off = (size_t)kt * kStageB;
@@ -172,8 +172,9 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
 #pragma unroll
     for (int i = 0; i < NB; i++) dst[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
   };
-  i32x8 ra[PD][2];
-  i32x4 rb[PD][NB];
+  constexpr int RING = PD + 1;
+  i32x8 ra[RING][2];
+  i32x4 rb[RING][NB];
 #pragma unroll
   for (int p = 0; p < PD; p++) {
     load_a(min(p, last), ra[p]);
@@ -183,11 +184,13 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   __syncthreads();
 
   const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int n_groups = (n_stages + PD - 1) / PD;
+  const int n_groups = (n_stages + RING - 1) / RING;
   for (int grp = 0; grp < n_groups; grp++) {
 #pragma unroll
-    for (int q = 0; q < PD; q++) {
-      const int kt = grp * PD + q;
+    for (int q = 0; q < RING; q++) {
+      const int kt = grp * RING + q;
+      load_a(min(kt + PD, last), ra[(q + PD) % RING]);
+      load_b(min(kt + PD, last), rb[(q + PD) % RING]);
       const bool valid = kt < n_stages;
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
@@ -202,35 +205,46 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
           const int off = b_base + ((vrot(4 * g + u) ^ vswz(r16)) << 4);
 #pragma unroll
           for (int j = 0; j < MT; j++) {
-            if (j < live) {
-              const bf16x8 fb = __builtin_bit_cast(
-                  bf16x8, *reinterpret_cast<const i32x4*>(cur + j * 16 * ROWB + off));
-              acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0u, fb, acc[0][j], 0, 0, 0);
-              acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1u, fb, acc[1][j], 0, 0, 0);
-            }
+            const bf16x8 fb = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const i32x4*>(cur + j * 16 * ROWB + off));
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0u, fb, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1u, fb, acc[1][j], 0, 0, 0);
           }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < MT; j++) {
-          if (j < live) {
-            const int sw = (r16 ^ (2 * j + r16h)) & 7;
-            const char* rowp = cur + j * 16 * kStageB + b_base;
-            const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
-                                  *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
-            acc[0][j] = M::mma(a0, fb, acc[0][j]);
-            acc[1][j] = M::mma(a1, fb, acc[1][j]);
-          }
+          const int sw = (r16 ^ (2 * j + r16h)) & 7;
+          const char* rowp = cur + j * 16 * kStageB + b_base;
+          const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
+                                *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
+          acc[0][j] = M::mma(a0, fb, acc[0][j]);
+          acc[1][j] = M::mma(a1, fb, acc[1][j]);
         }
       }
-      // the token chunk of stage kt+1 (ring slot (q+1) % PD) into the other
-      // LDS buffer, then refill slot q with stage kt+PD
-      stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % PD]);
-      load_a(min(kt + PD, last), ra[q]);
-      load_b(min(kt + PD, last), rb[q]);
+      // the token chunk of stage kt+1 (ring slot (q+1) % RING) into the
+      // other LDS buffer
+      stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % RING]);
       __syncthreads();
     }
   }
+}
+
+// A tile holding at most half of BM positions runs the main loop over BM / 2
+// columns only (a block-uniform choice between two fully unrolled loops):
+// Zipf-routed prefill tiles are 46% full on average, and the MFMAs, LDS reads
+// and token loads of the all-padding half are skipped.
+template <int MODE, int BM, int WN, int PD>
+__device__ __forceinline__ void run_mainloop(int mt, const char* const* a_rows,
+                                             const char* const* b_rows, int n_stages, char* lds,
+                                             f32x4 (*acc)[BM / 16]) {
+  if constexpr (BM / 2 >= 32 * WN) {
+    if (mt <= BM / 2) {
+      tile_mainloop<MODE, BM / 2, WN, PD, BM / 16>(a_rows, b_rows, n_stages, lds, acc);
+      return;
+    }
+  }
+  tile_mainloop<MODE, BM, WN, PD, BM / 16>(a_rows, b_rows, n_stages, lds, acc);
 }
 
 // ------------------------------------------------------------------- w13
@@ -277,8 +291,7 @@ __global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM, WN, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), (tl.mt + 15) >> 4,
-                                  lds, acc);
+  run_mainloop<MODE, BM, WN, PD>(tl.mt, a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
 
   float cs = 1.0f;
   if (is_fp8(MODE)) {
@@ -356,8 +369,7 @@ __global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < MT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<MODE, BM, WN, PD>(a_rows, b_rows, (int)(row_bytes / kStageB), (tl.mt + 15) >> 4,
-                                  lds, acc);
+  run_mainloop<MODE, BM, WN, PD>(tl.mt, a_rows, b_rows, (int)(row_bytes / kStageB), lds, acc);
 
   float cs = 1.0f;
   if (MODE == MOE_FP8_E4M3) {
