@@ -109,12 +109,15 @@ constexpr int stage_lds_bytes() {
 template <int MODE, int BM, int WN, int PD, int MTA>
 __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const char* const* b_rows,
                                               int n_stages, char* lds, f32x4 (*acc)[MTA]) {
-  static_assert(BM / 16 <= MTA && BM % (32 * WN) == 0, "tile shape");
+  static_assert(BM / 16 <= MTA && (BM % (32 * WN) == 0 || BM == 16 * WN), "tile shape");
   constexpr bool VIA = MODE == kFp8ViaBf16;
   typedef TileMma<VIA ? MOE_FP8_E4M3 : MODE> M;
   constexpr int ROWB = VIA ? 2 * kStageB : kStageB;  // LDS bytes per token row
   constexpr int B_BYTES = stage_lds_bytes<MODE, BM>();
-  constexpr int NB = BM / (32 * WN);     // token rows staged per thread
+  // token rows staged per thread; a stage of fewer than 32*WN rows is staged
+  // by the threads with r0 < BM only (whole waves)
+  constexpr int NB = BM >= 32 * WN ? BM / (32 * WN) : 1;
+  constexpr bool ALL_STAGE = BM >= 32 * WN;
   constexpr int MT = BM / 16;            // column tiles
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -135,6 +138,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
     }
   }
   auto stage_b = [&](char* buf, const i32x4* src) {
+    if (!ALL_STAGE && r0 >= BM) return;
 #pragma unroll
     for (int i = 0; i < NB; i++) {
       if (VIA) {
@@ -168,6 +172,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
                     *reinterpret_cast<const i32x4*>(a_rows[i] + off + ca1));
   };
   auto load_b = [&](int kt, i32x4* dst) {
+    if (!ALL_STAGE && r0 >= BM) return;
     const size_t off = (size_t)kt * kStageB;
 #pragma unroll
     for (int i = 0; i < NB; i++) dst[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
@@ -230,14 +235,21 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   }
 }
 
-// A tile holding at most half of BM positions runs the main loop over BM / 2
-// columns only (a block-uniform choice between two fully unrolled loops):
-// Zipf-routed prefill tiles are 46% full on average, and the MFMAs, LDS reads
-// and token loads of the all-padding half are skipped.
+// A tile holding at most a quarter or a half of BM positions runs the main
+// loop over BM / 4 or BM / 2 columns only (a block-uniform choice between
+// fully unrolled loops): Zipf-routed prefill tiles are 46% full on average,
+// and the MFMAs, LDS reads and token loads of the all-padding columns are
+// skipped.
 template <int MODE, int BM, int WN, int PD>
 __device__ __forceinline__ void run_mainloop(int mt, const char* const* a_rows,
                                              const char* const* b_rows, int n_stages, char* lds,
                                              f32x4 (*acc)[BM / 16]) {
+  if constexpr (BM == 128) {
+    if (mt <= BM / 4) {
+      tile_mainloop<MODE, BM / 4, WN, PD, BM / 16>(a_rows, b_rows, n_stages, lds, acc);
+      return;
+    }
+  }
   if constexpr (BM / 2 >= 32 * WN) {
     if (mt <= BM / 2) {
       tile_mainloop<MODE, BM / 2, WN, PD, BM / 16>(a_rows, b_rows, n_stages, lds, acc);

@@ -257,14 +257,17 @@ def test_align_sort_large_skewed():
     assert np.array_equal(inv.cpu().numpy(), ri)
 
 
-# Planted routing: expert counts on both sides of the 64- and 128-position
-# tile boundaries (0, 1, 63, 64, 127, 128, 129, 256, 640, ...), so experts
-# get exact, ragged and single-row last tiles.  The last layer has 8400
+# Planted routing: expert counts on both sides of the tile boundaries and of
+# the quarter / half / full main-loop widths (0, 1, 15-17, 31-33, 63-65, 96,
+# 127-129, 255-257, 540, ...), so experts get exact, ragged and single-row
+# last tiles.  The last layer has 8400
 # pairs: grouping by the chunked counting sort.
 PLANTED = [
     # name, T, H, E, k, I, mode, counts
-    ("fp8_planted_tile_edges", 1436, 256, 8, 1, 256, FP8, [0, 1, 127, 128, 129, 255, 256, 540]),
-    ("bf16_planted_tile_edges", 1436, 384, 8, 1, 128, BF16, [540, 256, 255, 129, 128, 127, 1, 0]),
+    ("fp8_planted_tile_edges", 1726, 256, 13, 1, 256, FP8,
+     [0, 1, 127, 128, 129, 255, 256, 540, 32, 33, 64, 65, 96]),
+    ("bf16_planted_tile_edges", 1726, 384, 13, 1, 128, BF16,
+     [96, 65, 64, 33, 32, 540, 256, 255, 129, 128, 127, 1, 0]),
     ("fp8_planted_tiles64", 700, 256, 16, 1, 256, FP8,
      [0, 1, 15, 16, 17, 63, 64, 65, 100, 127, 128, 33, 32, 31, 8, 0]),
     ("fp8_planted_chunked", 4200, 256, 8, 2, 128, FP8, [0, 256, 257, 511, 1024, 1280, 2520, 2552]),
