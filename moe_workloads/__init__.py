@@ -138,7 +138,11 @@ def make_layer(spec: LayerSpec, with_weights: bool = True):
         n_empty = int(round(0.1 * E))
         empty = np.sort(g.choice(E, size=n_empty, replace=False))
         logits[:, empty] = -np.inf
-    layer = dict(spec=spec, x=x, logits=np.ascontiguousarray(logits))
+    # the router weights as a router GEMM consumes them: one row per expert,
+    # in the activation type (the logits above use the unrounded draw)
+    wg_rows = np.ascontiguousarray(wg.T.astype(np.float32))
+    wg_act = wg_rows if mode == F32 else to_bf16_bits(wg_rows)
+    layer = dict(spec=spec, x=x, logits=np.ascontiguousarray(logits), wg=wg_act)
     if with_weights:
         kids = ss_w.spawn(2 * E)
         wdt = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}[mode]

@@ -61,6 +61,7 @@ def _load():
         lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
         lib.oracle_e4m3_decode_array.argtypes = [P, i64, P]
         lib.oracle_bf16_round_array.argtypes = [P, i64, P]
+        lib.oracle_router_logits.argtypes = [i32, i32, i32, i32, P, P, P]
         lib.oracle_topk_gating.argtypes = [P, i32, i32, i32, i32, P, P]
         lib.oracle_align_sort.argtypes = [P, i32, i32, i32, P, P, P, P]
         lib.oracle_act_quant.restype = ctypes.c_float
@@ -119,6 +120,19 @@ def bf16_to_f64(bits):
 
 
 # ---------------------------------------------------------------- steps
+def router_logits(mode, x, wg):
+    """logits[t][e] = sum_h x[t][h] * wg[e][h], summed exactly, rounded to fp32.
+    x [T,H] and wg [E,H] in the activation type (fp32, or bf16 bits)."""
+    x = _c(x, act_dtype(mode))
+    wg = _c(wg, act_dtype(mode))
+    T, H = x.shape
+    E, H2 = wg.shape
+    assert H2 == H
+    out = np.empty((T, E), np.float32)
+    _load().oracle_router_logits(mode, T, H, E, _p(x), _p(wg), _p(out))
+    return out
+
+
 def topk_gating(logits, k, renormalize=True):
     logits = _c(logits, np.float32)
     T, E = logits.shape

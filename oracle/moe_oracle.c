@@ -173,6 +173,27 @@ static inline void astore(void* a, int dt, size_t i, double v) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Step 0 (optional): the router's logits.                                    */
+/* Token routing starts from a score of every expert for every token          */
+/* (readmex.ai summary: routing is the first stage of the fused op).  The     */
+/* pages give no formula; Reading: a bias-free linear router, logits[t][e] =  */
+/* sum_h x[t][h] * wg[e][h], with wg stored in the activation type (bf16, or  */
+/* fp32 in fp32 mode) as one row per expert, summed exactly (double,          */
+/* ascending h) and rounded once to fp32.                                     */
+/* ------------------------------------------------------------------------ */
+void oracle_router_logits(int adt, int T, int H, int E, const void* x, const void* wg,
+                          float* logits) {
+#pragma omp parallel for schedule(static)
+  for (long te = 0; te < (long)T * E; te++) {
+    const long t = te / E, e = te % E;
+    double acc = 0.0;
+    for (int h = 0; h < H; h++)
+      acc += aval(x, adt, (size_t)t * H + h) * aval(wg, adt, (size_t)e * H + h);
+    logits[te] = (float)acc;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Step 1: top-k softmax gating.                                             */
 /* Token routing is the first stage of the fused op (readmex.ai summary;     */
 /* agentic-affairs.com "Swap-AB targets matrix execution on Hopper").        */

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import BF16, F32
 from oracle import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -109,3 +110,46 @@ def test_grouping_skewed_and_empty():
     assert counts[3] == T and counts[0] == 0 and counts[31] == 0
     assert np.array_equal(sorted_ids[:T], np.arange(T) * k)
     assert offsets[4] == T and offsets[E] == T * k
+
+
+# ------------------------------------------------------------ router logits
+def _to_act(a, mode):
+    a = np.ascontiguousarray(a, np.float32)
+    return a if mode == F32 else oracle.bf16_round(a.astype(np.float64)).reshape(a.shape)
+
+
+@pytest.mark.parametrize("mode", [F32, BF16])
+def test_router_logits_integer_inputs_exact(mode):
+    # small integers are exact in bf16 and their dot products are exact
+    # integers: the logits are known exactly (int64 matmul, a different code
+    # path from the oracle's double loop)
+    rng = np.random.default_rng(4)
+    T, H, E = 7, 96, 5
+    xi = rng.integers(-8, 9, (T, H))
+    wi = rng.integers(-8, 9, (E, H))
+    got = oracle.router_logits(mode, _to_act(xi, mode), _to_act(wi, mode))
+    assert got.dtype == np.float32 and got.shape == (T, E)
+    assert np.array_equal(got, (xi @ wi.T).astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", [F32, BF16])
+def test_router_logits_unit_vectors_pick_weights(mode):
+    # x = unit vector e_h  ->  logits[:, e] = wg[e, h]: pins the orientation
+    # (wg holds one row per expert) and the indexing of both operands
+    rng = np.random.default_rng(5)
+    H, E = 24, 6
+    wg = _to_act(rng.standard_normal((E, H)).astype(np.float32), mode)
+    x = _to_act(np.eye(H, dtype=np.float32), mode)
+    got = oracle.router_logits(mode, x, wg)
+    assert np.array_equal(got, oracle.to_f64(wg, mode).T.astype(np.float32))
+
+
+def test_router_logits_random_bf16_vs_float64_matmul():
+    # products of bf16 values are exact in double and, at these magnitudes,
+    # so are their sums: any summation order gives the same double
+    rng = np.random.default_rng(6)
+    T, H, E = 33, 512, 40
+    x = _to_act(rng.standard_normal((T, H)), BF16)
+    wg = _to_act(0.02 * rng.standard_normal((E, H)), BF16)
+    ref = (oracle.bf16_to_f64(x) @ oracle.bf16_to_f64(wg).T).astype(np.float32)
+    assert np.array_equal(oracle.router_logits(BF16, x, wg), ref)
