@@ -25,7 +25,10 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   separate figure;
   flushed      -- single calls timed alone (event pair around each call) after
                   reading a 1 GiB buffer that evicts L2 and the 256 MB MALL:
-                  median, p10 and p90, as a separate figure.
+                  median, p10 and p90, as a separate figure;
+  router       -- the layer run from the router weights instead of the logits
+                  (moe_fused_forward_router: the router GEMM x.wg^T in front),
+                  per step, and the router GEMM alone, as separate figures.
 """
 from __future__ import annotations
 
@@ -248,6 +251,28 @@ def main():
     graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     del graph
 
+    # the layer from the router weights (a separate figure): same steps with
+    # the router GEMM in front, and the router GEMM alone
+    wg = dev_act(L["wg"])
+    lg = torch.empty((spec.T, spec.E), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        moe.moe_fused_forward_router(x, wg, w13, s13, w2, s2, spec.k, out=out, ws=ws, logits=lg)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.moe_fused_forward_router(x, wg, w13, s13, w2, s2, spec.k, out=out, ws=ws, logits=lg)
+    torch.cuda.synchronize()
+    router_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ra, rb = new_event(), new_event()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    H_.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    H_.hipEventRecord(ctypes.c_void_p(ra), stream)
+    for _ in range(args.steps):
+        moe.moe_router_logits(x, wg, k=spec.k, ws=ws, logits=lg)
+    H_.hipEventRecord(ctypes.c_void_p(rb), stream)
+    torch.cuda.synchronize()
+    router_ms = elapsed_ms(ra, rb) / args.steps
+
     # single calls after an L2 / MALL flush (outside the timed region): the
     # flush only reads, so the timed call inherits no dirty lines to write back
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
@@ -268,7 +293,7 @@ def main():
         H_.hipEventSynchronize(ctypes.c_void_p(evs[-1]))
         stage_ms += [elapsed_ms(evs[i], evs[i + 1]) for i in range(moe.NUM_STAGE_EVENTS - 1)]
     stage_ms /= reps
-    for e in evs + [e for p in pairs + fpairs for e in p]:
+    for e in evs + [ra, rb] + [e for p in pairs + fpairs for e in p]:
         H_.hipEventDestroy(ctypes.c_void_p(e))
 
     active, layer_bytes, flops, w13_bytes, w13_flops = algorithmic(spec, counts)
@@ -305,6 +330,9 @@ def main():
         "layer_alg_bytes": layer_bytes,
         "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": spec.T / (graph_ms * 1e-3),
                          "layer_hbm_frac": layer_bytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "router": {"ms_per_step": router_step_ms,
+                   "tokens_per_s": spec.T / (router_step_ms * 1e-3),
+                   "router_gemm_ms": router_ms},
         "flushed": {"calls": len(fms), "ms_median": float(np.median(fms)),
                     "ms_p10": float(np.percentile(fms, 10)),
                     "ms_p90": float(np.percentile(fms, 90)),

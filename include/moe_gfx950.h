@@ -146,6 +146,30 @@ int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, co
                       int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* Router GEMM: logits[t][e] = sum_h x[t][h] * wg[e][h] with fp32
+ * accumulation, for the top-k gating (readmex.ai, "AWS details fused MoE
+ * kernel optimizations on SageMaker", summary: token routing is the first
+ * stage of the fused operation).
+ *   x      [T,H]  activation type (fp32 in F32 mode, bf16 otherwise), device
+ *   wg     [E,H]  the router weights, one row per expert, same type as x
+ *   logits [T,E]  fp32 out, row-major
+ * Products are exact (bf16 x bf16, or fp32 FMA in F32 mode) and summed in
+ * fp32, in an order that depends on the shape, so logits may differ from an
+ * exact sum by a few fp32 rounding steps of sum_h |x w|.  Uses the
+ * workspace of moe_workspace_bytes(s).  Null, misaligned (16 B) pointers or
+ * a small workspace give MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE. */
+int moe_router_logits(const moe_shape* s, const void* x, const void* wg, float* logits,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer from the token activations and the router weights:
+ * moe_router_logits followed by moe_fused_forward on its logits, enqueued
+ * on `stream`.  logits [T,E] (optional out, NULL = kept in the workspace)
+ * receives the router output the gating used. */
+int moe_fused_forward_router(const moe_shape* s, const void* x, const void* wg, const void* w13,
+                             const float* w13_scale, const void* w2, const float* w2_scale,
+                             void* out, float* logits, int32_t* topk_ids, float* topk_weights,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* Stage timing for profiling: identical to moe_fused_forward, and in
  * addition takes timestamps into events[i] (a hipEvent_t created by the
  * caller, or NULL to skip that point) at stage boundary i, so that the

@@ -36,7 +36,8 @@ class moe_shape(ctypes.Structure):
 
 EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string", "moe_topk_gating",
            "moe_align_sort", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_w2", "moe_combine",
-           "moe_fused_forward", "moe_fused_forward_events")
+           "moe_fused_forward", "moe_fused_forward_events", "moe_router_logits",
+           "moe_fused_forward_router")
 NUM_STAGE_EVENTS = 9
 
 
@@ -62,6 +63,8 @@ def lib():
         L.moe_grouped_gemm_w2.argtypes = [S, P, P, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P]
         L.moe_fused_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_router_logits.argtypes = [S, P, P, P, P, sz, P]
+        L.moe_fused_forward_router.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_fused_forward_events.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P,
                                                ctypes.POINTER(ctypes.c_void_p), i32]
         for name in EXPORTS[3:]:
@@ -206,6 +209,44 @@ def moe_fused_forward(x, logits, w13, w13_scale, w2, w2_scale, k, renormalize=Tr
                                    _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
                                    _ptr(topk_ids), _ptr(topk_weights), _ptr(ws), ws.numel(),
                                    _stream()), "moe_fused_forward")
+    return out
+
+
+def moe_router_logits(x, wg, E=None, k=1, ws=None, logits=None):
+    """Router GEMM: logits [T,E] fp32 = x [T,H] . wg [E,H]^T (fp32 or bf16
+    operands of the same type, fp32 accumulation)."""
+    T, H = x.shape
+    E_, H2 = wg.shape
+    assert H2 == H and (E is None or E == E_)
+    mode = MOE_F32 if x.dtype == torch.float32 else MOE_BF16
+    # the workspace depends only on T, H, E here; a minimal expert FFN shape
+    shape = make_shape(T, H, E_, min(k, E_), 128, mode)
+    ws = workspace(shape, x.device) if ws is None else ws
+    if logits is None:
+        logits = torch.empty((T, E_), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_logits(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(logits), _ptr(ws),
+                                   ws.numel(), _stream()), "moe_router_logits")
+    return logits
+
+
+def moe_fused_forward_router(x, wg, w13, w13_scale, w2, w2_scale, k, renormalize=True, out=None,
+                             ws=None, logits=None, topk_ids=None, topk_weights=None):
+    """The whole layer from x and the router weights wg [E,H] (activation
+    type); `logits` (optional [T,E] fp32) receives the router output."""
+    mode = mode_of(w13)
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    assert tuple(wg.shape) == (E, H) and wg.dtype == act_dtype(mode)
+    shape = make_shape(T, H, E, k, I, mode, renormalize)
+    ws = workspace(shape, x.device) if ws is None else ws
+    if out is None:
+        out = torch.empty((T, H), dtype=act_dtype(mode), device=x.device)
+    _check(lib().moe_fused_forward_router(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(w13),
+                                          _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
+                                          _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
+                                          _ptr(ws), ws.numel(), _stream()),
+           "moe_fused_forward_router")
     return out
 
 

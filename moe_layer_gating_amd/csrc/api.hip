@@ -35,8 +35,8 @@ inline long max_tiles_for(long n_pairs, int E, int bm) {
 // Offsets of the workspace regions for one shape.
 struct Layout {
   size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, tiles_big, chunk_counts, chunk_base,
-      rank, xq, hq, h, y, total;
-  long max_tiles, max_tiles_big;
+      rank, xq, hq, h, y, logits, rtiles, total;
+  long max_tiles, max_tiles_big, max_rtiles;
 };
 
 // Shape class: the many-token tiled GEMMs once experts receive 16 or more
@@ -84,6 +84,9 @@ Layout layout_for(const moe_shape& s) {
   L.hq = take(fp8 ? (size_t)np * s.I : 0);
   L.h = take((size_t)np * s.I * act_bytes(s.wdtype));
   L.y = take((size_t)np * s.H * 4);
+  L.max_rtiles = ((long)s.T + kRouterBM - 1) / kRouterBM;
+  L.logits = take((size_t)s.T * s.E * 4);
+  L.rtiles = take((size_t)(L.max_rtiles + 1) * sizeof(Tile));
   L.total = o;
   return L;
 }
@@ -284,6 +287,41 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
 
 namespace {
 
+int router_impl(const moe_shape* s, const void* x, const void* wg, float* logits, void* ws,
+                hipStream_t st) {
+  const Layout L = layout_for(*s);
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  return hip_status(launch_router_logits(s->wdtype, x, wg, s->T, s->H, s->E, logits,
+                                         at<Tile>(ws, L.rtiles), &ctrl->num_tiles_router,
+                                         (int)L.max_rtiles, st));
+}
+
+int check_router_args(const moe_shape* s, const void* x, const void* wg, const float* logits) {
+  if (!x || !wg) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wg) || (logits && !aligned16(logits)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_router_logits(const moe_shape* s, const void* x, const void* wg, float* logits, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!logits) return MOE_ERR_INVALID_ARG;
+  if ((rc = check_router_args(s, x, wg, logits))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  return router_impl(s, x, wg, logits, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
 int fused_impl(const moe_shape* s, const void* x, const float* logits, const void* w13,
                const float* w13_scale, const void* w2, const float* w2_scale, void* out,
                int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream,
@@ -388,6 +426,21 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
 }  // namespace
 
 extern "C" {
+
+int moe_fused_forward_router(const moe_shape* s, const void* x, const void* wg, const void* w13,
+                             const float* w13_scale, const void* w2, const float* w2_scale,
+                             void* out, float* logits, int32_t* topk_ids, float* topk_weights,
+                             void* ws, size_t ws_bytes, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  if ((rc = check_router_args(s, x, wg, logits))) return rc;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  float* lg = logits ? logits : at<float>(ws, layout_for(*s).logits);
+  if ((rc = router_impl(s, x, wg, lg, ws, reinterpret_cast<hipStream_t>(stream)))) return rc;
+  return fused_impl(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
+                    ws_bytes, stream, nullptr);
+}
 
 int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, const void* w13,
                       const float* w13_scale, const void* w2, const float* w2_scale, void* out,

@@ -16,6 +16,7 @@ constexpr int kRouteSmallMax = 256;  // pairs routed by the one-block front kern
 constexpr int kSortChunk = 1024;     // pairs per chunk of the many-pair grouping (one per thread)
 constexpr int kChunkSortMin = 8192;  // pairs from which the chunked grouping is used
 constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)
+constexpr int kRouterBM = 64;    // tokens per tile of the tiled router GEMM
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -55,7 +56,8 @@ struct Ctrl {
   uint32_t amax_h_bits;    // max |h| as fp32 bits
   int32_t num_tiles;       // tiles of <= kSkinnyBM positions written by the tile builder
   int32_t num_tiles_big;   // tiles of the many-token GEMMs
-  int32_t pad[60];
+  int32_t num_tiles_router;  // token tiles of the tiled router GEMM
+  int32_t pad[59];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl block is one 256-byte slot");
 
@@ -138,6 +140,12 @@ hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
                               int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
+// Router GEMM logits[t][e] = x[t] . wg[e] (fp32 accumulation); `tiles` holds
+// ceil(T / kRouterBM) entries and *num_tiles is written (tiled path only).
+bool router_uses_tiles(int mode, int T, int E);
+hipError_t launch_router_logits(int mode, const void* x, const void* wg, int T, int H, int E,
+                                float* logits, Tile* tiles, int32_t* num_tiles, int max_tiles,
+                                hipStream_t st);
 hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hipStream_t st);
 hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_bits, uint8_t* dst,
                              hipStream_t st);
