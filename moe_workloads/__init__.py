@@ -53,7 +53,8 @@ class LayerSpec:
     seed: int = 0
 
 
-# The five layer shapes the path is built for.
+# The five layer shapes the path is built for, plus the prefill dims in the
+# compute-bound regime.
 WORKLOADS = {
     "tiny_f32": LayerSpec("tiny_f32", 16, 128, 8, 2, 256, F32),
     "decode_bf16": LayerSpec("decode_bf16", 8, 4096, 8, 2, 14336, BF16),
@@ -62,6 +63,10 @@ WORKLOADS = {
     "decode_fp8_t16": LayerSpec("decode_fp8_t16", 16, 4096, 64, 8, 8192, FP8, draw_T=16),
     "prefill_fp8": LayerSpec("prefill_fp8", 4096, 7168, 256, 8, 2048, FP8, routing="zipf"),
     "mixed_fp8": LayerSpec("mixed_fp8", 512, 6144, 128, 8, 4096, FP8, routing="empty"),
+    # the prefill layer's dims at four times the tokens (mean 512 pairs per
+    # expert): the compute-bound regime, an extra labelled measurement
+    "prefill_fp8_t16k": LayerSpec("prefill_fp8_t16k", 16384, 7168, 256, 8, 2048, FP8,
+                                  routing="zipf"),
 }
 
 

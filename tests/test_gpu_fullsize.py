@@ -8,8 +8,9 @@ FP8 activation scale s_x are bit-exact against the CPU oracle everywhere.
   oracle computes the whole layer, so `out` is compared element by element
   (max|gpu - ref| / max|ref| <= 5e-3 bf16, 2e-2 FP8, ref = the oracle's
   output before its final rounding to bf16).
-* prefill FP8 layer (4096 tokens, 256 experts): the oracle's cost (about
-  1e12 multiply-adds for h alone) rules out the whole layer, so it checks
+* prefill FP8 layers (4096 tokens, and 16384 tokens for the compute-bound
+  regime; 256 experts): the oracle's cost (about 1e12 multiply-adds for h
+  alone at 4096 tokens) rules out the whole layer, so it checks
   sampled h rows (first, last and ragged-tail rows of the heaviest experts,
   single-pair experts), the exact amax(h) of the GPU's own h, and that the
   fused call's output equals the step-by-step entry points' output bit for
@@ -124,8 +125,9 @@ def _sample_positions(counts, offsets, rng):
     return np.array(sorted(pos), np.int64)
 
 
-def test_prefill_fp8_full_sampled():
-    L = _gen(wl.WORKLOADS["prefill_fp8"])
+@pytest.mark.parametrize("name", ["prefill_fp8", "prefill_fp8_t16k"])
+def test_prefill_fp8_full_sampled(name):
+    L = _gen(wl.WORKLOADS[name])
     s = L["spec"]
     D = upload(L)
     out, ids, w = _fused(D, s.k, s.T, s.H, FP8)
