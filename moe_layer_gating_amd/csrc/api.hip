@@ -322,13 +322,11 @@ int moe_router_logits(const moe_shape* s, const void* x, const void* wg, float* 
 
 namespace {
 
-int fused_impl(const moe_shape* s, const void* x, const float* logits, const void* w13,
-               const float* w13_scale, const void* w2, const float* w2_scale, void* out,
-               int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream,
-               void** events) {
-  int rc = moe_check_shape(s);
-  if (rc) return rc;
-  if (s->T == 0) return MOE_OK;
+// Argument checks of the fused entry points (shape already valid, T > 0).
+int check_fused_args(const moe_shape* s, const void* x, const float* logits, const void* w13,
+                     const float* w13_scale, const void* w2, const float* w2_scale,
+                     const void* out, const int32_t* topk_ids, const float* topk_weights,
+                     void* ws, size_t ws_bytes) {
   const bool fp8 = s->wdtype == MOE_FP8_E4M3;
   if (!x || !logits || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!w13_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
@@ -337,7 +335,20 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
       (topk_weights && !aligned16(topk_weights)) ||
       (fp8 && (!aligned16(w13_scale) || !aligned16(w2_scale))))
     return MOE_ERR_INVALID_ARG;
-  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  return check_ws(s, ws, ws_bytes);
+}
+
+int fused_impl(const moe_shape* s, const void* x, const float* logits, const void* w13,
+               const float* w13_scale, const void* w2, const float* w2_scale, void* out,
+               int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream,
+               void** events) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  const bool fp8 = s->wdtype == MOE_FP8_E4M3;
+  if ((rc = check_fused_args(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids,
+                             topk_weights, ws, ws_bytes)))
+    return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // boundaries 0-3 and 8 are marker events; 4/5 and 6/7 are the start / end
   // of the gate/up and down GEMM dispatches themselves
@@ -437,6 +448,10 @@ int moe_fused_forward_router(const moe_shape* s, const void* x, const void* wg, 
   if ((rc = check_router_args(s, x, wg, logits))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   float* lg = logits ? logits : at<float>(ws, layout_for(*s).logits);
+  // every argument of the layer is checked before the router is enqueued
+  if ((rc = check_fused_args(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids,
+                             topk_weights, ws, ws_bytes)))
+    return rc;
   if ((rc = router_impl(s, x, wg, lg, ws, reinterpret_cast<hipStream_t>(stream)))) return rc;
   return fused_impl(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
                     ws_bytes, stream, nullptr);

@@ -116,3 +116,28 @@ def test_invalid_pointers_rejected_before_launch(L):
     s0 = moe.make_shape(0, 256, 8, 2, 256, 2)
     assert L.moe_fused_forward(ctypes.byref(s0), good, good, good, good, good, good, good, None,
                                None, ws, moe.moe_workspace_bytes(s0), None) == 0
+
+
+def test_router_entry_points_reject_before_launch(L):
+    good = _fake(0x100000)
+    odd = _fake(0x100004)
+    s = moe.make_shape(4, 256, 8, 2, 256, 2)
+    S = ctypes.byref(s)
+    need = moe.moe_workspace_bytes(s)
+    ws = _fake(0x200000)
+    assert L.moe_router_logits(S, None, good, good, ws, need, None) == -1
+    assert L.moe_router_logits(S, good, odd, good, ws, need, None) == -1
+    assert L.moe_router_logits(S, good, good, None, ws, need, None) == -1
+    assert L.moe_router_logits(S, good, good, good, ws, need - 1, None) == -3
+    s0 = moe.make_shape(0, 256, 8, 2, 256, 2)
+    assert L.moe_router_logits(ctypes.byref(s0), good, good, good, ws, need, None) == 0
+    # the layer's arguments are checked before the router is enqueued: FP8
+    # without scales, a misaligned output, a null router matrix
+    assert L.moe_fused_forward_router(S, good, good, good, None, good, good, good, None, None,
+                                      None, ws, need, None) == -1
+    assert L.moe_fused_forward_router(S, good, good, good, good, good, good, odd, None, None,
+                                      None, ws, need, None) == -1
+    assert L.moe_fused_forward_router(S, good, None, good, good, good, good, good, None, None,
+                                      None, ws, need, None) == -1
+    assert L.moe_fused_forward_router(ctypes.byref(s0), good, good, good, good, good, good, good,
+                                      None, None, None, ws, need, None) == 0

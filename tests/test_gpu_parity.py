@@ -310,3 +310,25 @@ def test_planted_tile_edges(c):
     torch.cuda.synchronize()
     y_ref, _ = oracle.w2(mode, ref["h"], L["w2"], L["w2_scale"], ref["offsets"], k)
     assert rel_inf(y.cpu().numpy(), y_ref) <= (2e-4 if mode == FP8 else 1e-5)
+
+
+@pytest.mark.parametrize("c", [CASES[3], CASES[7], CASES[14], CASES[19]],
+                         ids=["bf16_small", "fp8_zipf", "fp8_tiles_ragged", "fp8_chunked_sort"])
+def test_fused_forward_full_softmax_weights(c):
+    # renormalize = 0: the selected experts keep their full-softmax
+    # probabilities (through every front-end path: one-block, per-expert
+    # grouping, chunked sort)
+    name, T, H, E, k, I, mode, routing = c
+    L, _ = case(c)
+    ref = oracle.forward(mode, L["x"], L["logits"], L["w13"], L["w13_scale"], L["w2"],
+                         L["w2_scale"], k, renormalize=False)
+    D = upload(L)
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    say("fused renormalize=0", name)
+    out = moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
+                                D["w2_scale"], k, renormalize=False, topk_weights=w)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(w.cpu().numpy() - ref["topk_weights"])) <= 1e-6
+    err = rel_inf(oracle.to_f64(act_to_numpy(out, mode), mode), ref["out_exact"])
+    say("  rel err", err)
+    assert err <= OUT_TOL[mode]
