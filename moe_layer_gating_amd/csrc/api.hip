@@ -205,7 +205,8 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
   const bool big = use_tiles(*s);
   MOE_TRY(launch_zero_words(reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
   if (big)
-    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big,
+                               &ctrl->num_tiles_big, st));
   else
     MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = x;
@@ -248,7 +249,8 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   Tile* tiles_big = at<Tile>(ws, L.tiles_big);
   const bool big = use_tiles(*s);
   if (big)
-    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big, &ctrl->num_tiles_big, st));
+    MOE_TRY(launch_build_tiles(expert_offsets, s->E, tiles_bm(*s), tiles_big,
+                               &ctrl->num_tiles_big, st));
   else
     MOE_TRY(launch_build_tiles(expert_offsets, s->E, kSkinnyBM, tiles, &ctrl->num_tiles, st));
   const void* b = h;
@@ -262,8 +264,9 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
     b = hq;
   }
   if (big)
-    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), b, w2, w2_scale, tiles_big, &ctrl->num_tiles_big,
-                            (int)L.max_tiles_big, s->H, s->I, amax_h, y, nullptr, nullptr, st));
+    MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), b, w2, w2_scale, tiles_big,
+                            &ctrl->num_tiles_big, (int)L.max_tiles_big, s->H, s->I, amax_h, y,
+                            nullptr, nullptr, st));
   else
     MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I,
                       amax_h, y, nullptr, nullptr, st));

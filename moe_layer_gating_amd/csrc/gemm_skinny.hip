@@ -131,7 +131,8 @@ constexpr int unroll_for() {
 // `brow` (this lane's token row, or nullptr for an empty column), over the
 // wave's steps [s0, s1).  U steps of loads are issued before their MFMAs.
 template <int MODE, int U>
-__device__ __forceinline__ f32x4 wave_dot(const char* __restrict__ arow, const char* __restrict__ brow,
+__device__ __forceinline__ f32x4 wave_dot(const char* __restrict__ arow,
+                                          const char* __restrict__ brow,
                                           int s0, int s1, int g) {
   typedef Step<MODE> S;
   constexpr int STEP_BYTES = S::KS * S::ES;
@@ -324,7 +325,8 @@ static void launch_w2_mode(long max_tiles, const char* b, const char* w2, const 
                            hipStream_t st) {
   constexpr int NW = waves_w2<MODE>();
   const long blocks = max_tiles * (H / 16);
-  launch_on(w2_skinny<MODE, NW, unroll_w2<MODE>()>, dim3(blocks), dim3(NW * 64), st, e0, e1, b, w2, w2_scale, tiles,
+  launch_on(w2_skinny<MODE, NW, unroll_w2<MODE>()>, dim3(blocks), dim3(NW * 64), st, e0, e1, b,
+            w2, w2_scale, tiles,
             ctrl, H, I, act_amax_bits, y);
 }
 

@@ -18,10 +18,11 @@
 //
 // Weights are streamed from HBM straight into registers in MFMA operand
 // layout (no LDS round trip: every weight byte is used by exactly one wave),
-// through a ring of kPD stages per wave, so that enough bytes are in flight
-// per CU to cover HBM latency.  The token tile is shared by the 4 waves: it
-// is prefetched into registers through a ring of the same depth and written
-// to a double-buffered LDS tile one stage before use.
+// prefetched kPD stages ahead through a ring of kPD + 1 register slots per
+// wave.  The token tile is shared by the block's waves: it is prefetched into
+// registers the same way and written to a double-buffered LDS tile one stage
+// before use.  Tiles holding at most a quarter or a half of BM positions run
+// a narrower copy of the main loop.
 //
 // LDS layout of a token stage: row r keeps its 16-byte chunk c at slot
 // c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7.  Eight consecutive rows read at
@@ -35,11 +36,11 @@
 // FP8 MFMA's are not.  A widened row is 256 bytes (16 chunks, chunk q holding
 // K values 8q .. 8q+7) and keeps chunk q at slot rot(q) ^ vswz(r), with
 // rot(q) = (q >> 1) | ((q & 1) << 3) and, for m = r & 15, vswz(r) = swz(m) |
-// (((m ^ (m >> 1)) & 1) << 3).  The 8 lanes staging one row store chunks 2c (then 2c+1), which
-// rot spreads over all 8 slots of a 128-byte bank row; a plain XOR layout
-// leaves them on 4 and the counters showed every access of the kernel
-// taking twice as long.  The fragment reads of 8, 16 and 32 consecutive
-// lanes, and the stores, hit distinct 16-byte bank groups.
+// (((m ^ (m >> 1)) & 1) << 3).  The 8 lanes staging one row store chunks 2c
+// (then 2c+1), which rot spreads over all 8 slots of a 128-byte bank row (a
+// plain XOR layout leaves them on 4: two-way store conflicts); the fragment
+// reads of 8, 16 and 32 consecutive lanes, and the stores, hit distinct
+// 16-byte bank groups.
 //
 // Launch order: block b takes tile b / NB and weight-row block b % NB, with
 // NB = (rows of the weight matrix) / (128*WN).  Blocks are dealt to the 8 XCDs
@@ -265,7 +266,8 @@ __device__ __forceinline__ void run_mainloop(int mt, const char* const* a_rows,
 // matching up feature, so a lane's accumulator rows 4g..4g+3 hold
 // gate/up/gate/up of features F + 8q + 2g and + 1.
 template <int MODE, int BM, int WN, int PD = kPD>
-__global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
+__global__ __launch_bounds__(256 * WN)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
     const char* __restrict__ b, const char* __restrict__ w13, const float* __restrict__ w13_scale,
     const int32_t* __restrict__ sorted_ids, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, const uint32_t* act_amax_bits,
@@ -346,7 +348,8 @@ __global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // -------------------------------------------------------------------- w2
 template <int MODE, int BM, int WN, int PD = kPD>
-__global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict__ b,
+__global__ __launch_bounds__(256 * WN)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict__ b,
                                                 const char* __restrict__ w2,
                                                 const float* __restrict__ w2_scale,
                                                 const Tile* __restrict__ tiles,

@@ -225,7 +225,8 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* c
 // One block of 256 threads.  Expert e with c = offsets[e+1]-offsets[e] pairs
 // contributes ceil(c / bm) tiles of at most bm consecutive sorted positions;
 // tiles are listed expert by expert.  The tile count goes to *num_tiles.
-__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
+__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                          int E,
                                                           int bm, Tile* __restrict__ tiles,
                                                           int32_t* num_tiles) {
   __shared__ int tmp[4];

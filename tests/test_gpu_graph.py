@@ -1,4 +1,4 @@
-"""The fused entry point captured in a HIP graph (torch.cuda.CUDAGraph) and
+"""The fused entry points captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: every replay, with eager work and synchronisations between the
 replays, must reproduce the eagerly launched result bit for bit.  The layer
 enqueues no memset and no host synchronisation, so it is capturable; this
@@ -23,7 +23,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+# the router entry point (router GEMM in front): its few-token and tiled paths
+ROUTER_CASES = [
+    ("graph_router_decode", 4, 512, 32, 8, 256, FP8, "uniform"),
+    ("graph_router_tiles", 300, 256, 128, 8, 128, FP8, "uniform"),
+]
+
+
+@pytest.mark.parametrize("c", CASES + ROUTER_CASES, ids=[c[0] for c in CASES + ROUTER_CASES])
 def test_graph_replays_match_eager(c):
     assert torch.cuda.is_available()
     name, T, H, E, k, I, mode, routing = c
@@ -33,10 +40,16 @@ def test_graph_replays_match_eager(c):
     ws = moe.workspace(shape)
     out = torch.empty((T, H), dtype=moe.act_dtype(mode), device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    router = name.startswith("graph_router")
+    wg = torch.from_numpy(L["wg"].view(np.int16)).view(torch.bfloat16).cuda() if router else None
 
     def step():
-        moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
-                              D["w2_scale"], k, out=out, ws=ws, topk_ids=ids)
+        if router:
+            moe.moe_fused_forward_router(D["x"], wg, D["w13"], D["w13_scale"], D["w2"],
+                                         D["w2_scale"], k, out=out, ws=ws, topk_ids=ids)
+        else:
+            moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
+                                  D["w2_scale"], k, out=out, ws=ws, topk_ids=ids)
 
     say("graph", name)
     step()
