@@ -310,9 +310,11 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int* t
 //   4. stable grouping: pair f lands at its expert's offset plus the number
 //      of earlier pairs routed to the same expert, so pairs keep ascending
 //      order inside each expert;
-//   5. FP8 (xq != nullptr): amax(x) over the block and the e4m3 codes of x.
-// Every control word is written here: amax_x (0 unless FP8), amax_h = 0 and
-// the tile counts.
+//   5. FP8 (xq != nullptr): amax(x) and the e4m3 codes of x, done by a second
+//      block of the same launch, concurrently with steps 1-4 (they share no
+//      data), so the two parts cost the longer of them rather than the sum.
+// Every control word is written here: amax_x (block 1 in FP8 mode, else 0),
+// amax_h = 0 and the tile counts.
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -327,54 +329,60 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   __shared__ float red[NW];
   const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
   const int n = T * k;
-  hist[t] = 0;
+  if (blockIdx.x == 0) {  // steps 1-4; in FP8 mode block 1 quantises x
+    hist[t] = 0;
 
-  // 1. gating
-  for (int tok = w; tok < T; tok += NW)
-    gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
-               wts + (size_t)tok * k, s_ids + tok * k);
-  __syncthreads();
+    // 1. gating
+    for (int tok = w; tok < T; tok += NW)
+      gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
+                 wts + (size_t)tok * k, s_ids + tok * k);
+    __syncthreads();
 
-  // 2. histogram and scans of the counts and of the tile counts
-  for (int f = t; f < n; f += 1024) atomicAdd(&hist[s_ids[f]], 1);
-  __syncthreads();
-  const int cnt = (t < E) ? hist[t] : 0;
-  const int nt = (cnt + bm - 1) / bm;
-  int total_pairs, total_tiles;
-  const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
-  const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
-  if (t < E) {
-    counts[t] = cnt;
-    offsets[t] = pre;
-    run[t] = pre;
-    // 3. tiles of this expert
-    for (int i = 0; i < nt; i++) {
-      Tile tl;
-      tl.e = t;
-      tl.p0 = pre + i * bm;
-      tl.mt = min(bm, cnt - i * bm);
-      tl.pad = 0;
-      tiles[tpre + i] = tl;
+    // 2. histogram and scans of the counts and of the tile counts
+    for (int f = t; f < n; f += 1024) atomicAdd(&hist[s_ids[f]], 1);
+    __syncthreads();
+    const int cnt = (t < E) ? hist[t] : 0;
+    const int nt = (cnt + bm - 1) / bm;
+    int total_pairs, total_tiles;
+    const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
+    const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
+    if (t < E) {
+      counts[t] = cnt;
+      offsets[t] = pre;
+      run[t] = pre;
+      // 3. tiles of this expert
+      for (int i = 0; i < nt; i++) {
+        Tile tl;
+        tl.e = t;
+        tl.p0 = pre + i * bm;
+        tl.mt = min(bm, cnt - i * bm);
+        tl.pad = 0;
+        tiles[tpre + i] = tl;
+      }
     }
-  }
-  if (t == 0) offsets[E] = n;
-  __syncthreads();
+    if (t == 0) offsets[E] = n;
+    __syncthreads();
 
-  // 4. stable grouping: pair f goes to its expert's offset plus the number of
-  // earlier pairs on the same expert (broadcast LDS reads, no atomics)
-  for (int f = t; f < n; f += 1024) {
-    const int e = s_ids[f];
-    int rank = 0;
-    for (int j = 0; j < f; j++) rank += (s_ids[j] == e);
-    const int pos = run[e] + rank;
-    sorted_ids[pos] = f;
-    if (inv_perm) inv_perm[f] = pos;
-  }
+    // 4. stable grouping: pair f goes to its expert's offset plus the number of
+    // earlier pairs on the same expert (broadcast LDS reads, no atomics)
+    for (int f = t; f < n; f += 1024) {
+      const int e = s_ids[f];
+      int rank = 0;
+      for (int j = 0; j < f; j++) rank += (s_ids[j] == e);
+      const int pos = run[e] + rank;
+      sorted_ids[pos] = f;
+      if (inv_perm) inv_perm[f] = pos;
+    }
 
-  // 5. FP8 activation quantisation (x is bf16, H a multiple of 128): four
-  // 16-byte loads in flight per thread
-  uint32_t amax_bits = 0u;
-  if (xq) {
+    if (t == 0) {
+      if (!xq) ctrl->amax_x_bits = 0u;
+      ctrl->amax_h_bits = 0u;
+      ctrl->num_tiles = total_tiles;
+      ctrl->num_tiles_big = 0;
+    }
+  } else {
+    // 5. FP8 activation quantisation (x is bf16, H a multiple of 128): four
+    // 16-byte loads in flight per thread
     const int n8 = T * H / 8;
     const i32x4* x4 = reinterpret_cast<const i32x4*>(x);
     float m = 0.f;
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; i++) a = fmaxf(a, red[i]);
-    amax_bits = __float_as_uint(a);
+    if (t == 0) ctrl->amax_x_bits = __float_as_uint(a);
     const float r = a > 0.f ? 448.0f / a : 1.0f;
     uint2* d2 = reinterpret_cast<uint2*>(xq);
     for (int i0 = t; i0 < n8; i0 += 4 * 1024) {
@@ -426,20 +434,15 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
       }
     }
   }
-  if (t == 0) {
-    ctrl->amax_x_bits = amax_bits;
-    ctrl->amax_h_bits = 0u;
-    ctrl->num_tiles = total_tiles;
-    ctrl->num_tiles_big = 0;
-  }
 }
 
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                               int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
                               const uint16_t* x, int H, uint8_t* xq, hipStream_t st) {
-  route_small_kernel<<<1, 1024, 0, st>>>(logits, T, E, k, renorm, ids, w, counts, offsets,
-                                         sorted_ids, inv_perm, bm, tiles, ctrl, x, H, xq);
+  route_small_kernel<<<xq ? 2 : 1, 1024, 0, st>>>(logits, T, E, k, renorm, ids, w, counts,
+                                                 offsets, sorted_ids, inv_perm, bm, tiles, ctrl,
+                                                 x, H, xq);
   return hipGetLastError();
 }
 
