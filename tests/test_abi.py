@@ -141,3 +141,23 @@ def test_router_entry_points_reject_before_launch(L):
                                       None, ws, need, None) == -1
     assert L.moe_fused_forward_router(ctypes.byref(s0), good, good, good, good, good, good, good,
                                       None, None, None, ws, need, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    # the product path has no fallback: without the HIP library every entry
+    # point raises instead of computing anything elsewhere
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libmoe_gfx950.so"))
+    with pytest.raises(moe.MoeError):
+        moe.lib()
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(moe.make_shape(4, 256, 8, 2, 256, 2))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
