@@ -333,6 +333,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[mode],
+        # the MFMA arithmetic of each GEMM (FP8 mode stores e4m3 weights and
+        # activations; its gate/up products run on the bf16 MFMA, exact for
+        # e4m3 values, its down projection on the FP8 MFMA)
+        "mfma_types": {"gate_up": "bf16 (e4m3 codes widened)" if mode == 2 else DTYPE_NAME[mode],
+                       "down": DTYPE_NAME[mode]},
         "data": "synthetic (seeded; moe_workloads recipe)",
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d I=%d" % (
             spec.name, spec.T, spec.H, spec.E, spec.k, spec.I), "T": spec.T, "H": spec.H,
