@@ -27,11 +27,31 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// LDS words of the per-wave scratch of gate_token's rank selection: the
+// token's logits (2 per lane), then k slot values and k slot experts.
+constexpr int kRankMaxE = 2 * kWave;
+constexpr int kGateScratch = kRankMaxE + 2 * 16;
+
+// Orders this wave's LDS accesses: every lane's earlier LDS writes are
+// complete and visible to the other lanes before any later access.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Top-k of one token by one whole wave; lanes 0..k-1 write slot `lane` to
-// ids_row / wts_row (and to lds_ids if given).
+// ids_row / wts_row (and to lds_ids if given).  With `scratch` (kGateScratch
+// words of LDS owned by this wave) and E <= kRankMaxE the selection is by
+// ranks: the row goes to LDS and every lane counts, for each of its (at most
+// two) logits, the experts ordered before it by (logit desc, index asc),
+// reading the row back four logits at a time (broadcast reads); the logit of
+// rank j < k is slot j.  That is one pass of independent comparisons instead
+// of k dependent wave-wide arg-max rounds, and selects the same experts.
 __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E, int k, int renorm,
                                            int32_t* __restrict__ ids_row,
-                                           float* __restrict__ wts_row, int* lds_ids) {
+                                           float* __restrict__ wts_row, int* lds_ids,
+                                           float* scratch = nullptr) {
   const int lane = lane_id();
   float v[kMaxPerLane];
   const int per_lane = (E + kWave - 1) / kWave;
@@ -47,6 +67,41 @@ __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E,
 
   float my_v = -INFINITY, top_v = 0.f;
   int my_e = 0;
+  if (scratch && E <= kRankMaxE) {
+    float* srow = scratch;
+    float* sv = scratch + kRankMaxE;
+    int* se = reinterpret_cast<int*>(scratch + kRankMaxE + 16);
+    wave_lds_sync();  // a previous token's reads of this scratch are done
+    // v[i] is -inf beyond E: such an entry has an index >= E, so it never
+    // ranks before a real expert, and its own rank is at least E >= k
+    srow[lane] = v[0];
+    srow[lane + kWave] = v[1];
+    wave_lds_sync();
+    int r0 = 0, r1 = 0;
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(srow);
+    for (int q = 0; q < (E + 3) / 4; q++) {
+      const f32x4 c = s4[q];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        r0 += better(c[u], 4 * q + u, v[0], lane);
+        r1 += better(c[u], 4 * q + u, v[1], lane + kWave);
+      }
+    }
+    if (lane < E && r0 < k) {
+      sv[r0] = v[0];
+      se[r0] = lane;
+    }
+    if (lane + kWave < E && r1 < k) {
+      sv[r1] = v[1];
+      se[r1] = lane + kWave;
+    }
+    wave_lds_sync();
+    top_v = sv[0];
+    if (lane < k) {
+      my_v = sv[lane];
+      my_e = se[lane];
+    }
+  } else {
   for (int j = 0; j < k; j++) {
     // best untaken candidate of this lane
     float bv = -INFINITY;
@@ -75,6 +130,7 @@ __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E,
       my_v = bv;
       my_e = be;
     }
+  }
   }
   // weights: exp(l - l_top) over the selected slots, divided by their sum
   // (renorm) or by the sum over every expert (top_v is the row maximum).
@@ -322,7 +378,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     Tile* __restrict__ tiles, Ctrl* ctrl, const uint16_t* __restrict__ x, int H,
     uint8_t* __restrict__ xq) {
   constexpr int NW = 16;
-  __shared__ int s_ids[kRouteSmallMax];
+  __shared__ __attribute__((aligned(16))) int s_ids[kRouteSmallMax];
+  __shared__ __attribute__((aligned(16))) float gscr[NW][kGateScratch];
   __shared__ int hist[1024];
   __shared__ int run[1024];  // offsets of the experts
   __shared__ int tmp[NW];
@@ -335,7 +392,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     // 1. gating
     for (int tok = w; tok < T; tok += NW)
       gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
-                 wts + (size_t)tok * k, s_ids + tok * k);
+                 wts + (size_t)tok * k, s_ids + tok * k, gscr[w]);
     __syncthreads();
 
     // 2. histogram and scans of the counts and of the tile counts
@@ -368,7 +425,12 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     for (int f = t; f < n; f += 1024) {
       const int e = s_ids[f];
       int rank = 0;
-      for (int j = 0; j < f; j++) rank += (s_ids[j] == e);
+      const int4* s4 = reinterpret_cast<const int4*>(s_ids);
+      for (int j = 0; j < f / 4; j++) {  // 16-byte reads every lane shares
+        const int4 q = s4[j];
+        rank += (q.x == e) + (q.y == e) + (q.z == e) + (q.w == e);
+      }
+      for (int j = f & ~3; j < f; j++) rank += (s_ids[j] == e);
       const int pos = run[e] + rank;
       sorted_ids[pos] = f;
       if (inv_perm) inv_perm[f] = pos;
@@ -382,17 +444,20 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     }
   } else {
     // 5. FP8 activation quantisation (x is bf16, H a multiple of 128): four
-    // 16-byte loads in flight per thread
+    // 16-byte loads in flight per thread; the first four are kept in
+    // registers for the encoding pass (the whole of x up to 32768 values)
     const int n8 = T * H / 8;
     const i32x4* x4 = reinterpret_cast<const i32x4*>(x);
     float m = 0.f;
-    for (int i0 = t; i0 < n8; i0 += 4 * 1024) {
-      i32x4 v[4];
+    i32x4 v0[4];
+    auto load4 = [&](int i0, i32x4* v) {
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int i = i0 + u * 1024;
         v[u] = (i < n8) ? x4[i] : i32x4{0, 0, 0, 0};
       }
+    };
+    auto amax4 = [&](const i32x4* v) {
 #pragma unroll
       for (int u = 0; u < 4; u++)
 #pragma unroll
@@ -401,6 +466,13 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
           m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(uu & 0xffffu))));
           m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(uu >> 16))));
         }
+    };
+    load4(t, v0);
+    amax4(v0);
+    for (int i0 = t + 4 * 1024; i0 < n8; i0 += 4 * 1024) {
+      i32x4 v[4];
+      load4(i0, v);
+      amax4(v);
     }
     m = wave_max(m);
     if (lane == 0) red[w] = m;
@@ -413,10 +485,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     uint2* d2 = reinterpret_cast<uint2*>(xq);
     for (int i0 = t; i0 < n8; i0 += 4 * 1024) {
       i32x4 v[4];
+      if (i0 == t) {
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const int i = i0 + u * 1024;
-        v[u] = (i < n8) ? x4[i] : i32x4{0, 0, 0, 0};
+        for (int u = 0; u < 4; u++) v[u] = v0[u];
+      } else {
+        load4(i0, v);
       }
 #pragma unroll
       for (int u = 0; u < 4; u++) {

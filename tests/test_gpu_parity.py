@@ -61,6 +61,13 @@ CASES = [
     # last chunk) inside the fused entry point
     ("fp8_tiles_chunked_sort", 1100, 256, 16, 8, 256, FP8, "zipf"),
     ("bf16_tiles_chunked_sort", 4200, 128, 64, 2, 128, BF16, "uniform"),
+    # the interface's largest expert count and top-k (E = 1024, k = 16): 256
+    # pairs, the most the one-block front kernel takes; 272 pairs, just past
+    # it; and 16 pairs per expert on average, the smallest mean that takes the
+    # tiled GEMMs, with the chunked grouping over all 1024 experts
+    ("bf16_max_E_k", 16, 128, 1024, 16, 128, BF16, "uniform"),
+    ("fp8_max_E_k_multi", 17, 128, 1024, 16, 128, FP8, "uniform"),
+    ("fp8_tiles_max_E", 1024, 128, 1024, 16, 128, FP8, "uniform"),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -234,6 +241,36 @@ def test_gating_ties_and_neginf():
         say("gating adversarial", kind)
         for renorm in (True, False):
             ids, w = moe.moe_topk_gating(torch.from_numpy(l).cuda(), k, renorm)
+            torch.cuda.synchronize()
+            rid, rw = oracle.topk_gating(l, k, renorm)
+            assert np.array_equal(ids.cpu().numpy(), rid)
+            assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+
+
+@pytest.mark.parametrize("E,k,T", [(64, 8, 32), (128, 8, 16), (100, 6, 20), (5, 5, 3), (8, 2, 16)])
+def test_fused_front_gating_ties_and_neginf(E, k, T):
+    """The fused entry point's one-block front kernel (T*k <= 256, few pairs
+    per expert) selects by ranks for E <= 128: ids bit-exact and weights within
+    1e-6 of the oracle on tie-heavy, -inf and signed-zero logits, with both
+    weight rules, and the grouping it writes matches the oracle's."""
+    rng = np.random.default_rng(E * 100 + k)
+    L = wl.make_layer(wl.scaled("front_%d_%d" % (E, k), T, 128, E, k, 128, BF16, seed=E + k))
+    D = upload(L)
+    for kind in range(3):
+        if kind == 0:
+            l = rng.integers(-2, 3, (T, E)).astype(np.float32)
+        elif kind == 1:
+            l = rng.standard_normal((T, E)).astype(np.float32)
+            if E - len(range(1, E, 3)) >= k:  # keep >= k finite entries per row
+                l[:, 1::3] = -np.inf
+        else:
+            l = rng.choice(np.array([0.0, -0.0, -1.0], np.float32), (T, E)).astype(np.float32)
+        for renorm in (True, False):
+            say("fused front gating E=%d k=%d kind=%d renorm=%d" % (E, k, kind, renorm))
+            ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            moe.moe_fused_forward(D["x"], torch.from_numpy(l).cuda(), D["w13"], None, D["w2"],
+                                  None, k, renormalize=renorm, topk_ids=ids, topk_weights=w)
             torch.cuda.synchronize()
             rid, rw = oracle.topk_gating(l, k, renorm)
             assert np.array_equal(ids.cpu().numpy(), rid)
