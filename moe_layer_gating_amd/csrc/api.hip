@@ -266,7 +266,7 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   if (big)
     MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), b, w2, w2_scale, tiles_big,
                             &ctrl->num_tiles_big, (int)L.max_tiles_big, s->H, s->I, amax_h, y,
-                            nullptr, nullptr, st));
+                            false, nullptr, nullptr, st));
   else
     MOE_TRY(launch_w2(s->wdtype, b, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, s->H, s->I,
                       amax_h, y, nullptr, nullptr, st));
@@ -283,7 +283,7 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
     return MOE_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return hip_status(
-      launch_combine(s->wdtype, y, inv_perm, topk_weights, s->T, s->H, s->k, out, st));
+      launch_combine(s->wdtype, y, false, inv_perm, topk_weights, s->T, s->H, s->k, out, st));
 }
 
 }  // extern "C"
@@ -425,14 +425,18 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
                               &ctrl->amax_h_bits, hq, st));
     bh = hq;
   }
+  // FP8 layers with many tokens per expert keep y in bf16 between the down
+  // projection and the aggregation (half the bytes of that round trip); the
+  // step entry points return fp32 y
+  const bool y_bf16 = fp8 && big;
   if (big)
     MOE_TRY(launch_w2_tiles(s->wdtype, tiles_bm(*s), bh, w2, w2_scale, tiles_big,
                             &ctrl->num_tiles_big, (int)L.max_tiles_big, H, I, &ctrl->amax_h_bits,
-                            y, ev(6), ev(7), st));
+                            y, y_bf16, ev(6), ev(7), st));
   else
     MOE_TRY(launch_w2(s->wdtype, bh, w2, w2_scale, tiles, ctrl, (int)L.max_tiles, H, I,
                       &ctrl->amax_h_bits, y, ev(6), ev(7), st));
-  MOE_TRY(launch_combine(s->wdtype, y, inv, wts, T, H, k, out, st));
+  MOE_TRY(launch_combine(s->wdtype, y, y_bf16, inv, wts, T, H, k, out, st));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

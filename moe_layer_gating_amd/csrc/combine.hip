@@ -5,13 +5,15 @@
 // agentic-affairs.com, "Triton improves the FP8 execution path").
 //   out[t][m] = sum_{j<k} w[t][j] * y[inv_perm[t*k+j]][m]
 // summed in fp32 in slot order j = 0..k-1 and rounded once; each output row
-// is written exactly once, by one thread per 4 consecutive features.
+// is written exactly once, by one thread per 4 consecutive features.  y is
+// fp32, or bf16 (YB: the FP8 fused path of many-token layers), widened
+// exactly before the sum.
 #include "moe_common.h"
 
 namespace moe {
 
-template <int MODE>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+template <int MODE, bool YB>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const float* __restrict__ w, int T, int H,
                                                       int k, int blocks_per_row,
@@ -23,7 +25,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < k; j++) {
     const float wj = w[(size_t)t * k + j];
     const int p = inv_perm[(size_t)t * k + j];
-    f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)p * H + m);
+    const size_t o = (size_t)p * H + m;
+    f32x4 v;
+    if (YB) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y) + o);
+      v = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+      v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o);
+    }
     acc += wj * v;
   }
   if (MODE == MOE_F32) {
@@ -36,15 +46,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,
-                          int H, int k, void* out, hipStream_t st) {
+hipError_t launch_combine(int mode, const void* y, bool y_bf16, const int32_t* inv_perm,
+                          const float* w, int T, int H, int k, void* out, hipStream_t st) {
   const int bpr = (H / 4 + 255) / 256;
   const long grid = (long)bpr * T;
   if (grid <= 0) return hipSuccess;
+  if (mode == MOE_F32 && y_bf16) return hipErrorInvalidValue;
   if (mode == MOE_F32)
-    combine_kernel<MOE_F32><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+    combine_kernel<MOE_F32, false><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+  else if (y_bf16)
+    combine_kernel<MOE_BF16, true><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
   else
-    combine_kernel<MOE_BF16><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+    combine_kernel<MOE_BF16, false><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
   return hipGetLastError();
 }
 

@@ -197,6 +197,11 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       const int kt = grp * RING + q;
       load_a(min(kt + PD, last), ra[(q + PD) % RING]);
       load_b(min(kt + PD, last), rb[(q + PD) % RING]);
+      // keeps this stage's MFMAs and the consumers of the stages in flight
+      // from being scheduled up against the loads just issued (measured: FP8
+      // down projection 1.5% faster; the widening gate/up loop runs better
+      // with the compiler's own interleaving)
+      if constexpr (!VIA) __builtin_amdgcn_sched_barrier(0);
       const bool valid = kt < n_stages;
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
@@ -230,6 +235,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       }
       // the token chunk of stage kt+1 (ring slot (q+1) % RING) into the
       // other LDS buffer
+      if constexpr (!VIA) __builtin_amdgcn_sched_barrier(0);
       stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % RING]);
       __syncthreads();
     }
@@ -347,7 +353,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
 }
 
 // -------------------------------------------------------------------- w2
-template <int MODE, int BM, int WN, int PD = kPD>
+// YB: y is stored in bf16 (the FP8 fused path; the scaled fp32 accumulators
+// rounded to nearest even), else in fp32.
+template <int MODE, int BM, int WN, bool YB, int PD = kPD>
 __global__ __launch_bounds__(256 * WN)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict__ b,
                                                 const char* __restrict__ w2,
@@ -355,7 +363,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict_
                                                 const Tile* __restrict__ tiles,
                                                 const int32_t* __restrict__ num_tiles, int H, int I,
                                                 const uint32_t* act_amax_bits,
-                                                float* __restrict__ y) {
+                                                void* __restrict__ y) {
   constexpr int ES = MODE == MOE_FP8_E4M3 ? 1 : 2;
   constexpr int MT = BM / 16;
   __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB];
@@ -395,12 +403,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict_
   for (int j = 0; j < MT; j++) {
     const int col = j * 16 + r16;
     if (col < tl.mt) {
-      float* yrow = y + (size_t)(tl.p0 + col) * H + nb * kTileN * WN + w * 32;
+      const size_t yo = (size_t)(tl.p0 + col) * H + nb * kTileN * WN + w * 32;
 #pragma unroll
       for (int i = 0; i < 2; i++) {
         f32x4 v = acc[i][j];
         if (MODE == MOE_FP8_E4M3) v *= cs;
-        *reinterpret_cast<f32x4*>(yrow + i * 16 + 4 * g) = v;
+        const size_t o = yo + i * 16 + 4 * g;
+        if (YB) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + o) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + o) = v;
+        }
       }
     }
   }
@@ -431,18 +446,18 @@ static void launch_tiles_w13_mode(long max_tiles, const char* b, const char* w13
               amax_h_bits);
 }
 
-template <int MODE, int BM>
+template <int MODE, int BM, bool YB>
 static void launch_tiles_w2_mode(long max_tiles, const char* b, const char* w2,
                                  const float* w2_scale, const Tile* tiles,
                                  const int32_t* num_tiles, int H, int I,
-                                 const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
+                                 const uint32_t* act_amax_bits, void* y, hipEvent_t e0,
                                  hipEvent_t e1, hipStream_t st) {
   if (tiles_wn(false, BM, H) == 2)
-    launch_on(w2_tiles<MODE, BM, 2>, dim3(max_tiles * (long)(H / (2 * kTileN))), dim3(512), st,
-              e0, e1, b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
+    launch_on(w2_tiles<MODE, BM, 2, YB>, dim3(max_tiles * (long)(H / (2 * kTileN))), dim3(512),
+              st, e0, e1, b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
   else
-    launch_on(w2_tiles<MODE, BM, 1>, dim3(max_tiles * (long)(H / kTileN)), dim3(256), st, e0, e1,
-              b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
+    launch_on(w2_tiles<MODE, BM, 1, YB>, dim3(max_tiles * (long)(H / kTileN)), dim3(256), st, e0,
+              e1, b, w2, w2_scale, tiles, num_tiles, H, I, act_amax_bits, y);
 }
 
 hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
@@ -472,22 +487,27 @@ hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
 
 hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, const float* w2_scale,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
-                           int I, const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
-                           hipEvent_t e1, hipStream_t st) {
+                           int I, const uint32_t* act_amax_bits, void* y, bool y_bf16,
+                           hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   const char* bb = reinterpret_cast<const char*>(b);
   const char* ww = reinterpret_cast<const char*>(w2);
-#define MOE_W2_TILES(MODE_, BM_)                                                                \
-  launch_tiles_w2_mode<MODE_, BM_>(max_tiles, bb, ww, w2_scale, tiles, num_tiles, H, I,         \
-                                   act_amax_bits, y, e0, e1, st)
+#define MOE_W2_TILES(MODE_, BM_, YB_)                                                           \
+  launch_tiles_w2_mode<MODE_, BM_, YB_>(max_tiles, bb, ww, w2_scale, tiles, num_tiles, H, I,    \
+                                        act_amax_bits, y, e0, e1, st)
+  if (y_bf16 && mode != MOE_FP8_E4M3) return hipErrorInvalidValue;
   if (mode == MOE_BF16 && bm == 64)
-    MOE_W2_TILES(MOE_BF16, 64);
+    MOE_W2_TILES(MOE_BF16, 64, false);
   else if (mode == MOE_BF16 && bm == 128)
-    MOE_W2_TILES(MOE_BF16, 128);
+    MOE_W2_TILES(MOE_BF16, 128, false);
+  else if (mode == MOE_FP8_E4M3 && bm == 64 && !y_bf16)
+    MOE_W2_TILES(MOE_FP8_E4M3, 64, false);
+  else if (mode == MOE_FP8_E4M3 && bm == 128 && !y_bf16)
+    MOE_W2_TILES(MOE_FP8_E4M3, 128, false);
   else if (mode == MOE_FP8_E4M3 && bm == 64)
-    MOE_W2_TILES(MOE_FP8_E4M3, 64);
+    MOE_W2_TILES(MOE_FP8_E4M3, 64, true);
   else if (mode == MOE_FP8_E4M3 && bm == 128)
-    MOE_W2_TILES(MOE_FP8_E4M3, 128);
+    MOE_W2_TILES(MOE_FP8_E4M3, 128, true);
   else
     return hipErrorInvalidValue;
 #undef MOE_W2_TILES

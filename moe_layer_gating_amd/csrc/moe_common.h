@@ -169,11 +169,13 @@ hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                             const uint32_t* act_amax_bits, void* h, uint32_t* amax_h_bits,
                             hipEvent_t e0, hipEvent_t e1, hipStream_t st);
+// y_bf16 (FP8 only): y is stored in bf16 instead of fp32.
 hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, const float* w2_scale,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
-                           int I, const uint32_t* act_amax_bits, float* y, hipEvent_t e0,
-                           hipEvent_t e1, hipStream_t st);
-hipError_t launch_combine(int mode, const float* y, const int32_t* inv_perm, const float* w, int T,
-                          int H, int k, void* out, hipStream_t st);
+                           int I, const uint32_t* act_amax_bits, void* y, bool y_bf16,
+                           hipEvent_t e0, hipEvent_t e1, hipStream_t st);
+// y [T*k,H] in sorted order, fp32 or (y_bf16, not in fp32 mode) bf16.
+hipError_t launch_combine(int mode, const void* y, bool y_bf16, const int32_t* inv_perm,
+                          const float* w, int T, int H, int k, void* out, hipStream_t st);
 
 }  // namespace moe

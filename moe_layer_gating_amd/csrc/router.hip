@@ -121,7 +121,7 @@ hipError_t launch_router_logits(int mode, const void* x, const void* wg, int T, 
     // wg takes the weight side of the down-projection kernel: E output
     // features (its "H"), reduction length H (its "I"); bf16, no scales
     return launch_w2_tiles(MOE_BF16, kRouterBM, xb, wb, nullptr, tiles, num_tiles, max_tiles, E,
-                           H, nullptr, logits, nullptr, nullptr, st);
+                           H, nullptr, logits, false, nullptr, nullptr, st);
   }
   const dim3 grid(E, (T + kRouterTokens - 1) / kRouterTokens);
   if (mode == MOE_F32)

@@ -369,3 +369,28 @@ def test_fused_forward_full_softmax_weights(c):
     err = rel_inf(oracle.to_f64(act_to_numpy(out, mode), mode), ref["out_exact"])
     say("  rel err", err)
     assert err <= OUT_TOL[mode]
+
+
+@pytest.mark.parametrize("c", [c for c in CASES if c[6] == FP8 and c[1] * c[4] >= 16 * c[3]],
+                         ids=lambda c: c[0])
+def test_fused_fp8_tiles_equals_steps(c):
+    """FP8 layers with many pairs per expert: the fused call keeps y in bf16
+    between the down projection and the aggregation.  Its output equals the
+    step entry points' (same kernels, same order) once the step API's fp32 y
+    is rounded to bf16 (nearest even) before moe_combine."""
+    name, T, H, E, k, I, mode, routing = c
+    L, ref = case(c)
+    D = upload(L)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    say("fused vs steps", name)
+    out = moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
+                                D["w2_scale"], k, topk_ids=ids, topk_weights=w)
+    counts, offsets, sorted_ids, inv = moe.moe_align_sort(ids, E)
+    h, sc = moe.moe_grouped_gemm_w13_swiglu(D["x"], D["w13"], D["w13_scale"], sorted_ids, offsets,
+                                            k)
+    y = moe.moe_grouped_gemm_w2(h, D["w2"], D["w2_scale"], offsets, sc, k)
+    y_b = y.to(torch.bfloat16).to(torch.float32)
+    out_steps = moe.moe_combine(y_b, inv, w, mode, E=E)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_steps.view(torch.int16))
