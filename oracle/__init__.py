@@ -212,8 +212,11 @@ def w2(mode, h, w2_, w2_scale, offsets, k, positions=None):
     return y, np.float32(s_h.value)
 
 
-def combine(mode, y, inv_perm, topk_weights):
-    """out[t] = sum_j w[t,j] * y[inv_perm[t*k+j]]; y float64 or float32."""
+def combine(mode, y, inv_perm, topk_weights, exact=False):
+    """out[t] = sum_j w[t,j] * y[inv_perm[t*k+j]]; y float64 or float32.
+
+    With ``exact`` (float64 y only) also returns the sums before their
+    rounding to the output type: (out, out_exact)."""
     w = _c(topk_weights, np.float32)
     T, k = w.shape
     H = y.shape[1]
@@ -224,7 +227,11 @@ def combine(mode, y, inv_perm, topk_weights):
         _load().oracle_combine_f32(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out))
     else:
         yy = _c(y, np.float64)
-        _load().oracle_combine(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out), None)
+        ex = np.empty((T, H), np.float64) if exact else None
+        _load().oracle_combine(mode, T, H, k, _p(yy), _p(inv), _p(w), _p(out), _p(ex))
+        if exact:
+            return out, ex
+    assert not exact, "exact sums need float64 y"
     return out
 
 

@@ -12,7 +12,9 @@ FP8 activation scale s_x are bit-exact against the CPU oracle everywhere.
   regime; 256 experts): the oracle's cost (about 1e12 multiply-adds for h
   alone at 4096 tokens) rules out the whole layer, so it checks
   sampled h rows (first, last and ragged-tail rows of the heaviest experts,
-  single-pair experts), the exact amax(h) of the GPU's own h, and that the
+  single-pair experts), the exact amax(h) of the GPU's own h, the output
+  of sampled tokens (down projection and aggregation run by the oracle on
+  the GPU's own h, whose e4m3 codes are decided on it), and that the
   fused call's output equals the step-by-step entry points' output bit for
   bit (with the step API's fp32 y rounded to bf16, as the fused FP8 path of
   many-token layers keeps it).  A prefill-shaped slice (H=7168, I=2048,
@@ -163,6 +165,25 @@ def test_prefill_fp8_full_sampled(name):
     say("  sampled h: step ratio %.3f, identical %.4f" % (ratio, np.mean(hg[pos] == href)))
     assert ratio <= 1.0
     assert np.mean(hg[pos] == href) > 0.99
+    # down projection and aggregation of sampled tokens at full size, from
+    # the GPU's own h (the e4m3 codes of h are decided on it, with the scale
+    # of its amax, checked above): tokens of the heaviest expert's first and
+    # last rows, of single-pair experts, and random tokens
+    rng = np.random.default_rng(5)
+    toks = set(rng.integers(0, s.T, 16).tolist())
+    e_max = int(np.argmax(rc))
+    toks.update([int(rs[ro[e_max]]) // s.k, int(rs[ro[e_max + 1] - 1]) // s.k])
+    toks.update(int(rs[ro[e]]) // s.k for e in np.where(rc == 1)[0][:4])
+    toks = np.array(sorted(toks), np.int64)
+    pairs = (toks[:, None] * s.k + np.arange(s.k)[None, :]).ravel()
+    say("  oracle down projection + aggregation of %d tokens" % len(toks))
+    y_s, s_h = oracle.w2(FP8, hg, L["w2"], L["w2_scale"], ro, s.k, positions=ri[pairs])
+    assert s_h == scales[1]
+    _, o_ref = oracle.combine(FP8, y_s, np.arange(pairs.size, dtype=np.int32), w[toks],
+                              exact=True)
+    err = rel_inf(oracle.to_f64(og[toks], FP8), o_ref)
+    say("  sampled out: rel err %.3g (tolerance %g)" % (err, OUT_TOL[FP8]))
+    assert err <= OUT_TOL[FP8]
 
 
 def test_prefill_shaped_slice_full():
