@@ -5,9 +5,9 @@
 // agentic-affairs.com, "Triton improves the FP8 execution path").
 //   out[t][m] = sum_{j<k} w[t][j] * y[inv_perm[t*k+j]][m]
 // summed in fp32 in slot order j = 0..k-1 and rounded once; each output row
-// is written exactly once, by one thread per 4 consecutive features.  y is
-// fp32, or bf16 (YB: the FP8 fused path of many-token layers), widened
-// exactly before the sum.
+// is written exactly once, by one thread per 8 consecutive features.  y is
+// fp32, or bf16 (YB: the FP8 fused path of many-token layers: one 16-byte
+// load per slot), widened exactly before the sum.
 #include "moe_common.h"
 
 namespace moe {
@@ -19,36 +19,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int k, int blocks_per_row,
                                                       void* __restrict__ out) {
   const int t = blockIdx.x / blocks_per_row;
-  const int m = ((blockIdx.x - t * blocks_per_row) * blockDim.x + threadIdx.x) * 4;
+  const int m = ((blockIdx.x - t * blocks_per_row) * blockDim.x + threadIdx.x) * 8;
   if (t >= T || m >= H) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; j++) {
     const float wj = w[(size_t)t * k + j];
     const int p = inv_perm[(size_t)t * k + j];
     const size_t o = (size_t)p * H + m;
-    f32x4 v;
+    f32x4 v0, v1;
     if (YB) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y) + o);
-      v = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + o);
+      v0 = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+      v1 = f32x4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                 __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
     } else {
-      v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o);
+      v0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o);
+      v1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o + 4);
     }
-    acc += wj * v;
+    a0 += wj * v0;
+    a1 += wj * v1;
   }
+  const size_t oo = (size_t)t * H + m;
   if (MODE == MOE_F32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * H + m) = acc;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + oo) = a0;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + oo + 4) = a1;
   } else {
-    uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-    uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * H + m) =
-        make_uint2(lo, hi);
+    const uint4 r = {(uint32_t)f32_to_bf16(a0[0]) | ((uint32_t)f32_to_bf16(a0[1]) << 16),
+                     (uint32_t)f32_to_bf16(a0[2]) | ((uint32_t)f32_to_bf16(a0[3]) << 16),
+                     (uint32_t)f32_to_bf16(a1[0]) | ((uint32_t)f32_to_bf16(a1[1]) << 16),
+                     (uint32_t)f32_to_bf16(a1[2]) | ((uint32_t)f32_to_bf16(a1[3]) << 16)};
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oo) = r;
   }
 }
 
 hipError_t launch_combine(int mode, const void* y, bool y_bf16, const int32_t* inv_perm,
                           const float* w, int T, int H, int k, void* out, hipStream_t st) {
-  const int bpr = (H / 4 + 255) / 256;
+  const int bpr = (H / 8 + 255) / 256;
   const long grid = (long)bpr * T;
   if (grid <= 0) return hipSuccess;
   if (mode == MOE_F32 && y_bf16) return hipErrorInvalidValue;

@@ -25,10 +25,14 @@ __device__ __forceinline__ float amax_to_scale(uint32_t bits) {
 }
 
 // max |src| over n bf16 values (n a multiple of 8, src 16-byte aligned); each
-// thread keeps four 16-byte loads in flight.
-__global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ src, long n8,
-                                                        uint32_t* amax_bits) {
-  __shared__ float part[4];
+// thread keeps four 16-byte loads in flight.  Blocks of 1024 threads and at
+// most 512 of them: every block ends with one access to the single amax
+// word, and those same-address accesses serialise (a probe on a 59 MB tensor:
+// 2048 blocks of 256 threads took 46 us, the same reads without the atomics
+// 28 us).
+__global__ __launch_bounds__(1024) void amax_bf16_kernel(const uint16_t* __restrict__ src, long n8,
+                                                         uint32_t* amax_bits) {
+  __shared__ float part[16];
   float m = 0.f;
   const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
   const long stride = (long)gridDim.x * blockDim.x;
@@ -53,17 +57,20 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restri
   __syncthreads();
   if (threadIdx.x == 0) {
     // read first: most blocks then skip the atomic on the single address
-    const uint32_t b = __float_as_uint(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
+    float mb = part[0];
+#pragma unroll
+    for (int i = 1; i < 16; i++) mb = fmaxf(mb, part[i]);
+    const uint32_t b = __float_as_uint(mb);
     if (b > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, b);
   }
 }
 
 hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hipStream_t st) {
   long n8 = n / 8;
-  long blocks = (n8 + 1023) / 1024;
-  if (blocks > 2048) blocks = 2048;
+  long blocks = (n8 + 1023) / 1024;  // small tensors still spread over every CU
+  if (blocks > 512) blocks = 512;
   if (blocks < 1) blocks = 1;
-  amax_bf16_kernel<<<(int)blocks, 256, 0, st>>>(src, n8, amax_bits);
+  amax_bf16_kernel<<<(int)blocks, 1024, 0, st>>>(src, n8, amax_bits);
   return hipGetLastError();
 }
 
