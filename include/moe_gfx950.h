@@ -136,6 +136,22 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
 int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
                 const float* topk_weights, void* out, void* stream);
 
+/* Dynamic per-tensor FP8 quantisation of an activation, the step the FP8
+ * mode applies to x before the gate/up projection and to h before the down
+ * projection (FP8 tensor scaling in the same pass as the matrix work:
+ * agentic-affairs.com, "Triton improves the FP8 execution path";
+ * codebridge-ai.com, "aws-moe-kernel-wgmma-triton-ttft", section "2.
+ * Backend routing").
+ *   a      [n]  bf16, device; n a positive multiple of 8
+ *   codes  [n]  OCP e4m3fn codes out: e4m3(fl32(a * fl32(448 / amax))),
+ *               rounded to nearest even, saturated to +-448
+ *   scales [2]  fp32 out: scales[0] = s = fl32(amax / 448), scales[1] = amax
+ *               = max |a| (amax = 0 gives s = 1 and multiplier 1)
+ * a holds no NaN (precondition).  Null or misaligned (16 B) pointers, or n
+ * not a positive multiple of 8, give MOE_ERR_INVALID_ARG; n = 0 returns
+ * MOE_OK with nothing enqueued. */
+int moe_act_quant_e4m3(const void* a, int64_t n, uint8_t* codes, float* scales, void* stream);
+
 /* The whole layer in one call: gating, grouping, (FP8: x quantisation),
  * gate/up + SwiGLU, (FP8: h quantisation), down projection and aggregation,
  * enqueued back to back on `stream`.  Every token row of `out` is written

@@ -36,6 +36,7 @@ class moe_shape(ctypes.Structure):
 
 EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string", "moe_topk_gating",
            "moe_align_sort", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_w2", "moe_combine",
+           "moe_act_quant_e4m3",
            "moe_fused_forward", "moe_fused_forward_events", "moe_router_logits",
            "moe_fused_forward_router")
 NUM_STAGE_EVENTS = 9
@@ -62,6 +63,7 @@ def lib():
         L.moe_grouped_gemm_w13_swiglu.argtypes = [S, P, P, P, P, P, P, P, P, sz, P]
         L.moe_grouped_gemm_w2.argtypes = [S, P, P, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P]
+        L.moe_act_quant_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
         L.moe_fused_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_router_logits.argtypes = [S, P, P, P, P, sz, P]
         L.moe_fused_forward_router.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
@@ -182,6 +184,18 @@ def moe_grouped_gemm_w2(h, w2, w2_scale, expert_offsets, act_scales, k, ws=None,
                                      _ptr(expert_offsets), _ptr(act_scales), _ptr(y), _ptr(ws),
                                      ws.numel(), _stream()), "moe_grouped_gemm_w2")
     return y
+
+
+def moe_act_quant_e4m3(a, codes=None, scales=None):
+    """Per-tensor e4m3 codes of a bf16 tensor: (codes uint8, scales [s, amax] fp32)."""
+    n = a.numel()
+    if codes is None:
+        codes = torch.empty(a.shape, dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(2, dtype=torch.float32, device=a.device)
+    _check(lib().moe_act_quant_e4m3(_ptr(a), n, _ptr(codes), _ptr(scales), _stream()),
+           "moe_act_quant_e4m3")
+    return codes, scales
 
 
 def moe_combine(y, inv_perm, topk_weights, mode, E=None, I=128, out=None):

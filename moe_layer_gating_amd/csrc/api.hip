@@ -273,6 +273,21 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
   return MOE_OK;
 }
 
+int moe_act_quant_e4m3(const void* a, int64_t n, uint8_t* codes, float* scales, void* stream) {
+  if (n == 0) return MOE_OK;
+  if (n < 0 || n % 8 || !a || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // scales[1] takes the amax bits (integer atomics on fp32 patterns), then
+  // the value they encode; scales[0] the scale
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(scales + 1);
+  MOE_TRY(launch_zero_words(amax_bits, 1, st));
+  MOE_TRY(launch_amax_bf16(reinterpret_cast<const uint16_t*>(a), (long)n, amax_bits, st));
+  MOE_TRY(launch_quant_e4m3(reinterpret_cast<const uint16_t*>(a), (long)n, amax_bits, codes, st));
+  MOE_TRY(launch_finish_scale(scales, st));
+  return MOE_OK;
+}
+
 int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
                 const float* topk_weights, void* out, void* stream) {
   int rc = moe_check_shape(s);

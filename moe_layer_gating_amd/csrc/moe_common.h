@@ -74,19 +74,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// fp32 -> OCP e4m3fn code, round to nearest even, saturating to +-448.
-// Normal range: drop 20 fraction bits of the fp32 pattern with a
-// nearest-even carry (the carry may bump the exponent) and rebias 127 -> 7.
-// Below 2^-6: the value is an integer multiple of 2^-9 after rounding.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fabsf(v);
-  if (!(a <= 448.0f)) return (a != a) ? (sign | 0x7fu) : (sign | 0x7eu);
-  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  uint32_t x = u & 0x7fffffffu;
-  x += 0x7ffffu + ((x >> 20) & 1u);
-  return sign | ((x >> 20) - (120u << 3));
+// Eight bf16 values times r as eight OCP e4m3fn codes (element i in byte i):
+// fl32(v * r), rounded to nearest even and saturated to +-448 (subnormals
+// kept).  gfx950's v_cvt_pk_fp8_f32 rounds to nearest even in the OCP format;
+// the clamp to +-448 in front of it makes it saturate, and with it the
+// conversion was checked equal, on every non-NaN fp32 input, to a software
+// encoder written from the format's definition (drop 20 fraction bits with a
+// nearest-even carry and rebias 127 -> 7; below 2^-6, round v * 2^9 to an
+// integer).  NaN inputs are outside the contract (x and h hold no NaN).
+__device__ __forceinline__ uint2 bf16x8_to_e4m3x8(i32x4 v, float r) {
+  float f[8];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t u = (uint32_t)v[q];
+    f[2 * q] = __builtin_amdgcn_fmed3f(bf16_to_f32((uint16_t)(u & 0xffffu)) * r, -448.0f, 448.0f);
+    f[2 * q + 1] = __builtin_amdgcn_fmed3f(bf16_to_f32((uint16_t)(u >> 16)) * r, -448.0f, 448.0f);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
 // ----------------------------------------------------------------- wave ops
@@ -150,6 +158,8 @@ hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hi
 hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_bits, uint8_t* dst,
                              hipStream_t st);
 hipError_t launch_write_scales(const Ctrl* ctrl, float* act_scales, hipStream_t st);
+// scales[0] = amax / 448 (or 1) from the amax bits in scales[1].
+hipError_t launch_finish_scale(float* scales, hipStream_t st);
 // Grouped GEMMs.  `b` is the token-side operand: x (fp32/bf16) or the e4m3
 // codes of x (FP8) for w13; h (fp32/bf16) or the codes of h (FP8) for w2.
 // `act_amax_bits` (FP8 only) points at amax of that activation as fp32 bits.

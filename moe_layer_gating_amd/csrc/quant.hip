@@ -74,19 +74,6 @@ hipError_t launch_amax_bf16(const uint16_t* src, long n, uint32_t* amax_bits, hi
   return hipGetLastError();
 }
 
-__device__ __forceinline__ uint2 quant8(i32x4 v, float r) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    uint32_t u = (uint32_t)v[q], u2 = (uint32_t)v[q + 2];
-    lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u & 0xffffu)) * r) << (16 * q);
-    lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u >> 16)) * r) << (16 * q + 8);
-    hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 & 0xffffu)) * r) << (16 * q);
-    hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 >> 16)) * r) << (16 * q + 8);
-  }
-  return make_uint2(lo, hi);
-}
-
 // codes = e4m3(bf16 * 448/amax); 8 values per 16-byte load, four loads in
 // flight per thread.
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(const uint16_t* __restrict__ src, long n8,
@@ -106,7 +93,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const uint16_t* __restr
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const long i = i0 + u * stride;
-      if (i < n8) d2[i] = quant8(v[u], r);
+      if (i < n8) d2[i] = bf16x8_to_e4m3x8(v[u], r);
     }
   }
 }
@@ -118,6 +105,20 @@ hipError_t launch_quant_e4m3(const uint16_t* src, long n, const uint32_t* amax_b
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   quant_e4m3_kernel<<<(int)blocks, 256, 0, st>>>(src, n8, amax_bits, dst);
+  return hipGetLastError();
+}
+
+// scales = {amax / 448 (1 if amax = 0), amax}, from amax bits held in
+// scales[1] by the amax pass
+__global__ void finish_scale_kernel(float* scales) {
+  if (threadIdx.x == 0) {
+    const uint32_t b = __float_as_uint(scales[1]);
+    scales[0] = amax_to_scale(b);
+  }
+}
+
+hipError_t launch_finish_scale(float* scales, hipStream_t st) {
+  finish_scale_kernel<<<1, 64, 0, st>>>(scales);
   return hipGetLastError();
 }
 

@@ -494,16 +494,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int i = i0 + u * 1024;
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int q = 0; q < 2; q++) {
-          const uint32_t u0 = (uint32_t)v[u][q], u2 = (uint32_t)v[u][q + 2];
-          lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u0 & 0xffffu)) * r) << (16 * q);
-          lo |= f32_to_e4m3(bf16_to_f32((uint16_t)(u0 >> 16)) * r) << (16 * q + 8);
-          hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 & 0xffffu)) * r) << (16 * q);
-          hi |= f32_to_e4m3(bf16_to_f32((uint16_t)(u2 >> 16)) * r) << (16 * q + 8);
-        }
-        if (i < n8) d2[i] = make_uint2(lo, hi);
+        if (i < n8) d2[i] = bf16x8_to_e4m3x8(v[u], r);
       }
     }
   }

@@ -118,6 +118,19 @@ def test_invalid_pointers_rejected_before_launch(L):
                                None, ws, moe.moe_workspace_bytes(s0), None) == 0
 
 
+def test_act_quant_rejects_before_launch(L):
+    good = _fake(0x100000)
+    odd = _fake(0x100004)
+    assert L.moe_act_quant_e4m3(None, 64, good, good, None) == -1
+    assert L.moe_act_quant_e4m3(good, 64, None, good, None) == -1
+    assert L.moe_act_quant_e4m3(good, 64, good, None, None) == -1
+    assert L.moe_act_quant_e4m3(odd, 64, good, good, None) == -1
+    assert L.moe_act_quant_e4m3(good, 64, good, odd, None) == -1
+    assert L.moe_act_quant_e4m3(good, 12, good, good, None) == -1  # not a multiple of 8
+    assert L.moe_act_quant_e4m3(good, -8, good, good, None) == -1
+    assert L.moe_act_quant_e4m3(good, 0, good, good, None) == 0  # nothing enqueued
+
+
 def test_router_entry_points_reject_before_launch(L):
     good = _fake(0x100000)
     odd = _fake(0x100004)

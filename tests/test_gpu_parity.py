@@ -277,6 +277,47 @@ def test_fused_front_gating_ties_and_neginf(E, k, T):
             assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
 
 
+def _act_quant_case(bits):
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    codes, sc = moe.moe_act_quant_e4m3(x)
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle.act_quant(bits, BF16)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    got = sc.cpu().numpy()
+    assert got[0] == rs  # bit-exact scale
+    assert got[1] == np.float32(np.max(np.abs(oracle.to_f64(bits, BF16))))
+
+
+def test_act_quant_every_finite_bf16():
+    """The per-tensor e4m3 quantisation step (x before the gate/up
+    projection, h before the down projection): codes and scale bit-exact
+    against the oracle's codec, over every finite bf16 value (amax 2^128 -
+    2^120 makes the smallest values subnormal or zero codes), then over the
+    same values rescaled so that every bf16 binade lands on the codes."""
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[(allb & 0x7F80) != 0x7F80]
+    bits = np.concatenate([finite, np.zeros((-finite.size) % 8, np.uint16)])
+    say("act quant: %d finite bf16 values" % finite.size)
+    _act_quant_case(bits)
+    # the values of exponent field e (|v| in [2^(e-127), 2^(e-126))) with
+    # amax set by a single 2^(e-127+8) entry: codes over the whole range
+    for e in (1, 60, 120, 127, 140, 200, 246):
+        man = np.arange(256, dtype=np.uint16)
+        vals = np.concatenate([(e << 7) | (man & 0x7F), 0x8000 | (e << 7) | (man & 0x7F)])
+        top = np.array([min(e + 8, 254) << 7], np.uint16)
+        b = np.concatenate([vals, top, np.zeros(7, np.uint16)]).astype(np.uint16)
+        _act_quant_case(b)
+
+
+def test_act_quant_zero_and_random():
+    _act_quant_case(np.zeros(64, np.uint16))  # amax 0: scale 1, codes 0
+    rng = np.random.default_rng(9)
+    for sigma in (1e-3, 1.0, 300.0):
+        v = (rng.standard_normal(4096 * 8) * sigma).astype(np.float32)
+        bits = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        _act_quant_case(bits)
+
+
 def test_align_sort_large_skewed():
     rng = np.random.default_rng(8)
     T, k, E = 4096, 8, 256
