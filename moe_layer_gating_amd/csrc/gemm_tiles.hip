@@ -206,6 +206,9 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
       const char* cur = lds + (kt & 1) * B_BYTES;
+      // the non-widening loop raises its wave priority over its MFMA burst
+      // (16k-token FP8 down projection 2% faster; the widening loop slower)
+      if constexpr (!VIA) __builtin_amdgcn_s_setprio(1);
       if (VIA) {
         // MFMA u: the lane's codes 8u .. 8u+7 of its 32 (K values
         // 32g + 8u ..), i.e. bf16 chunk 4g + u of the token row
@@ -233,6 +236,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
           acc[1][j] = M::mma(a1, fb, acc[1][j]);
         }
       }
+      if constexpr (!VIA) __builtin_amdgcn_s_setprio(0);
       // the token chunk of stage kt+1 (ring slot (q+1) % RING) into the
       // other LDS buffer
       if constexpr (!VIA) __builtin_amdgcn_sched_barrier(0);
