@@ -435,3 +435,45 @@ def test_fused_fp8_tiles_equals_steps(c):
     out_steps = moe.moe_combine(y_b, inv, w, mode, E=E)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out_steps.view(torch.int16))
+
+
+def _random_shapes(n, seed=2024):
+    """Seeded layer shapes within the interface's limits, across the shape
+    classes: one-block and many-pair fronts, few-token and tiled GEMMs
+    (64- and 128-position tiles), every mode and routing recipe."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        mode = int(rng.integers(0, 3))
+        E = int(rng.choice([1, 3, 8, 17, 32, 64, 100]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 5, 33, 100, 257, 600, 1500]))
+        H = 128 * int(rng.integers(1, 4))
+        I = 128 * int(rng.integers(1, 5))
+        routing = str(rng.choice(["uniform", "zipf", "empty"])) if E >= 10 else "uniform"
+        out.append(("rand%02d" % i, T, H, E, k, I, mode, routing))
+    return out
+
+
+RANDOM = _random_shapes(24)
+
+
+@pytest.mark.parametrize("c", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shape_sweep(c):
+    name, T, H, E, k, I, mode, routing = c
+    L = wl.make_layer(wl.scaled(name, T, H, E, k, I, mode, routing=routing, seed=7 + len(name)))
+    ref = oracle.forward(mode, L["x"], L["logits"], L["w13"], L["w13_scale"], L["w2"],
+                         L["w2_scale"], k)
+    D = upload(L)
+    out = torch.full((T, H), float("nan"), dtype=moe.act_dtype(mode), device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    say("random shape", c)
+    moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"], D["w2_scale"], k,
+                          out=out, topk_ids=ids)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
+    og = oracle.to_f64(act_to_numpy(out, mode), mode)
+    assert not np.isnan(og).any()
+    err = rel_inf(og, ref["out_exact"])
+    say("  rel err", err)
+    assert err <= OUT_TOL[mode]
