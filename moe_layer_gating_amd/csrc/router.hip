@@ -9,9 +9,10 @@
 // removes the caller's separate GEMM launch in front of the layer.
 //
 // Two shapes of work:
-//   * few tokens or an expert count that is not a multiple of 128: one wave
-//     per (expert, group of up to 16 tokens), fp32 FMAs on 16-byte runs, the
-//     wave then adds its 64 partial sums per token;
+//   * few tokens or an expert count that is not a multiple of 128: one block
+//     of 8 waves per (expert, group of up to 16 tokens); each wave takes an
+//     eighth of the row (fp32 FMAs on 16-byte runs) and adds its 64 partial
+//     sums per token, then the 8 wave sums are added in wave order;
 //   * otherwise the many-token tiled GEMM of the down projection, with wg as
 //     the weight matrix of a single expert (E rows, K = H) and the tokens in
 //     tiles of 64: bf16 MFMAs, whose products are exact and whose sums are
@@ -45,28 +46,32 @@ struct Run<MOE_BF16> {
   }
 };
 
-constexpr int kRouterTokens = 16;  // tokens per wave of the few-token kernel
+constexpr int kRouterTokens = 16;  // tokens per block of the few-token kernel
+constexpr int kRouterWaves = 8;    // waves per block, each on 1/8 of the row
 
-// grid (E, ceil(T / 16)), one wave per block.  Lane l takes the 16-byte
-// runs l, l + 64, ... of the rows (H is a multiple of 128, so runs never
-// straddle the row end).
+// grid (E, ceil(T / 16)), kRouterWaves waves per block.  Wave w takes the
+// columns [w H / 8, (w + 1) H / 8); its lane l the 16-byte runs l, l + 64, ...
+// of that range (H is a multiple of 128, so H / 8 is a multiple of 16 and
+// runs never straddle a range end).  Eight times the waves of one wave per
+// (expert, token group): a decode-sized router is latency-bound.
 template <int MODE>
-__global__ __launch_bounds__(64) void router_small_kernel(const char* __restrict__ x,
-                                                          const char* __restrict__ wg, int T,
-                                                          int H, int E,
-                                                          float* __restrict__ logits) {
+__global__ __launch_bounds__(kRouterWaves * 64) void router_small_kernel(
+    const char* __restrict__ x, const char* __restrict__ wg, int T, int H, int E,
+    float* __restrict__ logits) {
   typedef Run<MODE> R;
   constexpr int ES = 16 / R::N;
+  __shared__ float part[kRouterWaves][kRouterTokens];
   const int e = blockIdx.x, t0 = blockIdx.y * kRouterTokens;
   const int nt = min(kRouterTokens, T - t0);
-  const int lane = threadIdx.x;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int kb = w * (H / kRouterWaves), ke = kb + H / kRouterWaves;
   const size_t row = (size_t)H * ES;
   const char* wrow = wg + (size_t)e * row;
   const char* xrow = x + (size_t)t0 * row;
   float acc[kRouterTokens];
 #pragma unroll
   for (int i = 0; i < kRouterTokens; i++) acc[i] = 0.f;
-  for (int h0 = lane * R::N; h0 < H; h0 += kWave * R::N) {
+  for (int h0 = kb + lane * R::N; h0 < ke; h0 += kWave * R::N) {
     float w[R::N];
     R::load(wrow + (size_t)h0 * ES, w);
 #pragma unroll
@@ -83,8 +88,15 @@ __global__ __launch_bounds__(64) void router_small_kernel(const char* __restrict
   for (int i = 0; i < kRouterTokens; i++) {
     if (i < nt) {
       const float s = wave_sum(acc[i]);
-      if (lane == 0) logits[(size_t)(t0 + i) * E + e] = s;
+      if (lane == 0) part[w][i] = s;
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    float s = part[0][threadIdx.x];
+#pragma unroll
+    for (int q = 1; q < kRouterWaves; q++) s += part[q][threadIdx.x];
+    logits[(size_t)(t0 + threadIdx.x) * E + e] = s;
   }
 }
 
@@ -125,9 +137,9 @@ hipError_t launch_router_logits(int mode, const void* x, const void* wg, int T, 
   }
   const dim3 grid(E, (T + kRouterTokens - 1) / kRouterTokens);
   if (mode == MOE_F32)
-    router_small_kernel<MOE_F32><<<grid, 64, 0, st>>>(xb, wb, T, H, E, logits);
+    router_small_kernel<MOE_F32><<<grid, kRouterWaves * 64, 0, st>>>(xb, wb, T, H, E, logits);
   else
-    router_small_kernel<MOE_BF16><<<grid, 64, 0, st>>>(xb, wb, T, H, E, logits);
+    router_small_kernel<MOE_BF16><<<grid, kRouterWaves * 64, 0, st>>>(xb, wb, T, H, E, logits);
   return hipGetLastError();
 }
 
