@@ -21,24 +21,49 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int t = blockIdx.x / blocks_per_row;
   const int m = ((blockIdx.x - t * blocks_per_row) * blockDim.x + threadIdx.x) * 8;
   if (t >= T || m >= H) return;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; j++) {
-    const float wj = w[(size_t)t * k + j];
-    const int p = inv_perm[(size_t)t * k + j];
-    const size_t o = (size_t)p * H + m;
-    f32x4 v0, v1;
-    if (YB) {
-      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + o);
-      v0 = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-      v1 = f32x4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
-                 __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
-    } else {
-      v0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o);
-      v1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o + 4);
+  // every slot's position and weight first, then every slot's y row: two
+  // dependent round trips instead of two per slot (k <= 16)
+  int p[16];
+  float wj[16];
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    if (j < k) {
+      p[j] = inv_perm[(size_t)t * k + j];
+      wj[j] = w[(size_t)t * k + j];
     }
-    a0 += wj * v0;
-    a1 += wj * v1;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (YB) {
+    uint4 u[16];  // raw bf16 rows, widened exactly at the sum
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (j < k)
+        u[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) +
+                                               (size_t)p[j] * H + m);
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (j < k) {  // slot order j = 0..k-1
+        const f32x4 v0 = {__uint_as_float(u[j].x << 16), __uint_as_float(u[j].x & 0xffff0000u),
+                          __uint_as_float(u[j].y << 16), __uint_as_float(u[j].y & 0xffff0000u)};
+        const f32x4 v1 = {__uint_as_float(u[j].z << 16), __uint_as_float(u[j].z & 0xffff0000u),
+                          __uint_as_float(u[j].w << 16), __uint_as_float(u[j].w & 0xffff0000u)};
+        a0 += wj[j] * v0;
+        a1 += wj[j] * v1;
+      }
+  } else {
+    f32x4 v0[16], v1[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (j < k) {
+        const size_t o = (size_t)p[j] * H + m;
+        v0[j] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o);
+        v1[j] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(y) + o + 4);
+      }
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (j < k) {  // slot order j = 0..k-1
+        a0 += wj[j] * v0[j];
+        a1 += wj[j] * v1[j];
+      }
   }
   const size_t oo = (size_t)t * H + m;
   if (MODE == MOE_F32) {
