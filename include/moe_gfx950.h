@@ -26,8 +26,9 @@
  *  - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 16), 0 <= T, T*k < 2^31,
  *    H and I positive multiples of 128 (MOE_ERR_UNSUPPORTED otherwise),
  *    every device pointer 16-byte aligned.
- *  - Preconditions the device does not check (violations are undefined):
- *    logits hold no NaN and at least k non-(-inf) entries per row;
+ *  - Preconditions the device does not check (violations are undefined,
+ *    except that a NaN logit is read as -inf, which keeps every expert id in
+ *    range): logits hold no NaN and at least k non-(-inf) entries per row;
  *    topk_ids lie in [0, E); sorted_ids / expert_offsets / inv_perm are the
  *    outputs of moe_align_sort for the same ids.
  *  - Results are deterministic: routing outputs are bit-identical run to run
@@ -86,25 +87,77 @@ size_t moe_workspace_bytes(const moe_shape* s);
 /* Host only.  Static description of a status code. */
 const char* moe_status_string(int status);
 
-/* Top-k softmax gating (token routing).
- * logits [T,E] fp32 in; topk_ids [T,k] int32 and topk_weights [T,k] fp32 out.
- * Slot j holds the expert with the (j+1)-th largest logit; equal logits go
- * to the lower expert index; -0 equals +0.  Weights: exp(l - l_max) over
- * the selected experts divided by their sum (renormalize = 1) or by the sum
- * over all experts (renormalize = 0). */
+/* Host only.  Where the fused entry points leave the routing of a call
+ * inside the caller's workspace: byte offsets from the start of `ws` (of
+ * this shape) of
+ *   topk_ids [T,k] int32, topk_weights [T,k] fp32 (written there only when
+ *     the caller passes NULL for those outputs),
+ *   expert_counts [E], expert_offsets [E+1], sorted_ids [T*k], inv_perm
+ *     [T*k] (int32, always written),
+ * each with the meaning of moe_align_sort's outputs.  They hold the call's
+ * values once the stream has passed it and until the next call that uses
+ * the same workspace.  Returns a moe_status (out == NULL: invalid). */
+typedef struct {
+  size_t topk_ids, topk_weights, expert_counts, expert_offsets, sorted_ids, inv_perm;
+} moe_routing_offsets;
+int moe_workspace_routing(const moe_shape* s, moe_routing_offsets* out);
+
+/* Top-k softmax gating: the token routing that opens the fused operation
+ * (readmex.ai, "AWS details fused MoE kernel optimizations on SageMaker, up
+ * to 10% throughput gain", summary; agentic-affairs.com, "Swap-AB targets
+ * matrix execution on Hopper": routing, data shuffling and the expert
+ * calculations in one batched GPU operation).  The pages name the stage but
+ * not its rule; the rule below is the softmax top-k this library implements.
+ *   logits       [T,E] fp32 in, row-major
+ *   topk_ids     [T,k] int32 out: slot j holds the expert with the (j+1)-th
+ *                largest logit; equal logits go to the lower expert index;
+ *                -0 equals +0
+ *   topk_weights [T,k] fp32 out: exp(l - l_max) over the selected experts
+ *                divided by their sum (renormalize = 1) or by the sum over
+ *                all E experts (renormalize = 0)
+ * Null or misaligned pointers, or T, E, k outside the limits, give
+ * MOE_ERR_INVALID_ARG with nothing enqueued.  A NaN logit (a precondition
+ * violation) is read as -inf, so the ids stay inside [0, E). */
 int moe_topk_gating(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
                     int32_t* topk_ids, float* topk_weights, void* stream);
 
-/* Grouping of pairs by expert ("data shuffling").
- * expert_counts[e] = number of pairs routed to e; expert_offsets = exclusive
- * prefix sum of the counts ([E+1], offsets[E] = T*k); sorted_ids [T*k] lists
- * the flat pair indices by expert ascending and, inside an expert, by pair
- * index ascending; inv_perm [T*k] (may be NULL) is its inverse. */
+/* Host only.  Bytes of device workspace moe_align_sort needs for T tokens,
+ * top-k and E experts (0 when T, E, k are outside the limits).  The
+ * workspace must be 256-byte aligned. */
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/* Grouping of the (token, slot) pairs by expert: the "data shuffling" stage
+ * of the fused operation (readmex.ai, "AWS details fused MoE kernel
+ * optimizations on SageMaker, up to 10% throughput gain", summary), whose
+ * per-expert batch sizes are data dependent (explore.n1n.ai,
+ * "Mixture-of-Experts Kernel Engineering on Amazon SageMaker AI", section
+ * "The Core Bottlenecks of MoE Inference on H200 GPUs").
+ *   topk_ids       [T,k] int32 in, every id in [0, E)
+ *   expert_counts  [E] int32 out: pairs routed to expert e
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of the counts,
+ *                  expert_offsets[E] = T*k
+ *   sorted_ids     [T*k] int32 out: flat pair indices f = t*k + j by expert
+ *                  ascending and, inside an expert, by f ascending
+ *   inv_perm       [T*k] int32 out (may be NULL): inv_perm[sorted_ids[p]] = p
+ *   ws, ws_bytes   device workspace of moe_align_sort_workspace_bytes
+ *                  bytes, 256-byte aligned, caller-owned
+ * The kernels are chosen by the pair count exactly as the fused entry point
+ * chooses them (one block up to 256 pairs, one block per expert below 8192,
+ * a chunked counting sort from 8192 on), so both run the same grouping.
+ * Errors: as moe_topk_gating; a missing, misaligned or small workspace gives
+ * MOE_ERR_WORKSPACE. */
 int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
-                   int32_t* inv_perm, void* stream);
+                   int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Expert gate/up projection with SwiGLU, grouped over experts.
+/* Expert gate/up projection with SwiGLU, grouped over experts: the first
+ * half of the expert network calculation of the fused operation (readmex.ai,
+ * "AWS details fused MoE kernel optimizations on SageMaker, up to 10%
+ * throughput gain", summary), with the large expert dimension on the matrix
+ * unit's row side for few-token batches (codebridge-ai.com,
+ * "aws-moe-kernel-wgmma-triton-ttft", section "1. Matrix swap") and the FP8
+ * tensor scales folded into the same pass (agentic-affairs.com, "Triton
+ * improves the FP8 execution path").
  * For sorted position p (pair f = sorted_ids[p], token t = f / k, expert e
  * with offsets[e] <= p < offsets[e+1]):
  *   g_n = x[t] . w13[e][n],  u_n = x[t] . w13[e][I+n]    (fp32 accumulation)
@@ -120,7 +173,18 @@ int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w
                                 const int32_t* expert_offsets, void* h, float* act_scales,
                                 void* ws, size_t ws_bytes, void* stream);
 
-/* Expert down projection, grouped over experts, unweighted.
+/* Expert down projection, grouped over experts, unweighted: the second half
+ * of the expert network calculation (readmex.ai, "AWS details fused MoE
+ * kernel optimizations on SageMaker, up to 10% throughput gain", summary),
+ * with the FP8 scales applied to the fp32 accumulators in the same pass
+ * (codebridge-ai.com, "aws-moe-kernel-wgmma-triton-ttft", section "2.
+ * Backend routing": scaling and matmul not as discrete steps).
+ * h is in sorted order, so the position p alone names its expert (through
+ * expert_offsets); no sorted_ids argument is needed.
+ * h [T*k,I] activation type in, sorted order; w2 [E,H,I]; w2_scale [E] fp32
+ * (FP8 only); act_scales [4] fp32 in as written by
+ * moe_grouped_gemm_w13_swiglu (FP8 only; only act_scales[3] is read);
+ * ws / ws_bytes as for moe_workspace_bytes(s).
  *   y[p][m] = h[p] . w2[e][m] (fp32 accumulation), e the expert of position p.
  *   FP8: h is quantised per tensor with the scale derived from
  *        act_scales[3] = amax(h) (codes e4m3(h * 448/amax)), and y is scaled
@@ -130,9 +194,15 @@ int moe_grouped_gemm_w2(const moe_shape* s, const void* h, const void* w2, const
                         const int32_t* expert_offsets, const float* act_scales, float* y,
                         void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted aggregation: out[t][m] = sum_{j<k} topk_weights[t][j] *
- * y[inv_perm[t*k+j]][m], summed in fp32 in slot order and rounded once to
- * the activation type. */
+/* Expert aggregation, the last stage of the fused FP8 pass
+ * (agentic-affairs.com, "Triton improves the FP8 execution path";
+ * codebridge-ai.com, "aws-moe-kernel-wgmma-triton-ttft", section "2. Backend
+ * routing"): out[t][m] = sum_{j<k} topk_weights[t][j] * y[inv_perm[t*k+j]][m],
+ * summed in fp32 in slot order and rounded once to the activation type.
+ * y [T*k,H] fp32 in (sorted order), inv_perm [T*k] int32, topk_weights [T,k]
+ * fp32, out [T,H] activation type out; every row of out is written once.
+ * Errors: null or misaligned pointers or a bad shape (MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED), nothing enqueued. */
 int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
                 const float* topk_weights, void* out, void* stream);
 
@@ -152,11 +222,19 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
  * MOE_OK with nothing enqueued. */
 int moe_act_quant_e4m3(const void* a, int64_t n, uint8_t* codes, float* scales, void* stream);
 
-/* The whole layer in one call: gating, grouping, (FP8: x quantisation),
- * gate/up + SwiGLU, (FP8: h quantisation), down projection and aggregation,
- * enqueued back to back on `stream`.  Every token row of `out` is written
- * exactly once.  topk_ids / topk_weights are optional outputs (NULL = kept
- * in the workspace). */
+/* The whole layer in one call, the single batched operation that merges
+ * routing, data shuffling and the expert calculations (readmex.ai, "AWS
+ * details fused MoE kernel optimizations on SageMaker, up to 10% throughput
+ * gain", summary): gating, grouping, (FP8: x quantisation), gate/up +
+ * SwiGLU, (FP8: h quantisation), down projection and aggregation, enqueued
+ * back to back on `stream`, with no host synchronisation.  Every token row
+ * of `out` is written exactly once.
+ *   x [T,H], logits [T,E] fp32, w13 [E,2I,H], w13_scale [E] (FP8), w2
+ *   [E,H,I], w2_scale [E] (FP8), out [T,H]; topk_ids / topk_weights are
+ *   optional outputs (NULL = kept in the workspace, see
+ *   moe_workspace_routing); ws of moe_workspace_bytes(s) bytes.
+ * Errors: as the step entry points, all checked before anything is
+ * enqueued. */
 int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, const void* w13,
                       const float* w13_scale, const void* w2, const float* w2_scale, void* out,
                       int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,

@@ -34,11 +34,19 @@ class moe_shape(ctypes.Structure):
                 ("renormalize", ctypes.c_int32)]
 
 
-EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string", "moe_topk_gating",
+class moe_routing_offsets(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("topk_ids", "topk_weights", "expert_counts",
+                                                "expert_offsets", "sorted_ids", "inv_perm")]
+
+
+EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string",
+           "moe_align_sort_workspace_bytes", "moe_workspace_routing", "moe_topk_gating",
            "moe_align_sort", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_w2", "moe_combine",
            "moe_act_quant_e4m3",
            "moe_fused_forward", "moe_fused_forward_events", "moe_router_logits",
            "moe_fused_forward_router")
+# host-only calls whose return type is not a moe_status
+_NON_STATUS = ("moe_workspace_bytes", "moe_status_string", "moe_align_sort_workspace_bytes")
 NUM_STAGE_EVENTS = 9
 
 
@@ -58,8 +66,11 @@ def lib():
         L.moe_workspace_bytes.restype = sz
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_align_sort_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_align_sort_workspace_bytes.restype = sz
+        L.moe_workspace_routing.argtypes = [S, ctypes.POINTER(moe_routing_offsets)]
         L.moe_topk_gating.argtypes = [P, i32, i32, i32, i32, P, P, P]
-        L.moe_align_sort.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.moe_align_sort.argtypes = [P, i32, i32, i32, P, P, P, P, P, sz, P]
         L.moe_grouped_gemm_w13_swiglu.argtypes = [S, P, P, P, P, P, P, P, P, sz, P]
         L.moe_grouped_gemm_w2.argtypes = [S, P, P, P, P, P, P, P, sz, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P]
@@ -69,8 +80,9 @@ def lib():
         L.moe_fused_forward_router.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_fused_forward_events.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P,
                                                ctypes.POINTER(ctypes.c_void_p), i32]
-        for name in EXPORTS[3:]:
-            getattr(L, name).restype = ctypes.c_int
+        for name in EXPORTS:
+            if name not in _NON_STATUS:
+                getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -139,16 +151,54 @@ def moe_topk_gating(logits, k, renormalize=True, topk_ids=None, topk_weights=Non
     return topk_ids, topk_weights
 
 
-def moe_align_sort(topk_ids, E, with_inv=True):
+def moe_align_sort_workspace_bytes(T, k, E):
+    return lib().moe_align_sort_workspace_bytes(int(T), int(k), int(E))
+
+
+def moe_align_sort(topk_ids, E, with_inv=True, ws=None):
     T, k = topk_ids.shape
     dev = topk_ids.device
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     sorted_ids = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev) if with_inv else None
+    if ws is None:
+        n = moe_align_sort_workspace_bytes(T, k, E)
+        if n == 0:
+            raise MoeError("invalid grouping shape T=%d k=%d E=%d" % (T, k, E))
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
     _check(lib().moe_align_sort(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets),
-                                _ptr(sorted_ids), _ptr(inv), _stream()), "moe_align_sort")
+                                _ptr(sorted_ids), _ptr(inv), _ptr(ws), ws.numel(), _stream()),
+           "moe_align_sort")
     return counts, offsets, sorted_ids, inv
+
+
+def moe_workspace_routing(shape):
+    """Byte offsets of the routing arrays the fused entry points leave in a
+    workspace of `shape` (a moe_routing_offsets)."""
+    r = moe_routing_offsets()
+    _check(lib().moe_workspace_routing(ctypes.byref(shape), ctypes.byref(r)),
+           "moe_workspace_routing")
+    return r
+
+
+def routing_from_workspace(ws, T, E, k, H=128, I=128, mode=MOE_BF16):
+    """Views (no copies) of the grouping a fused call left in `ws`: counts
+    [E], offsets [E+1], sorted_ids [T*k], inv_perm [T*k] (int32), plus the
+    ids [T,k] and weights [T,k] slots (filled only when the call kept them in
+    the workspace).  H, I and mode must be the call's when they change the
+    workspace layout (they place only regions after these)."""
+    r = moe_workspace_routing(make_shape(T, H, E, k, I, mode))
+
+    def view(off, n, dt):
+        return ws[off:off + 4 * n].view(dt)
+
+    return dict(counts=view(r.expert_counts, E, torch.int32),
+                offsets=view(r.expert_offsets, E + 1, torch.int32),
+                sorted_ids=view(r.sorted_ids, T * k, torch.int32),
+                inv_perm=view(r.inv_perm, T * k, torch.int32),
+                topk_ids=view(r.topk_ids, T * k, torch.int32).view(T, k),
+                topk_weights=view(r.topk_weights, T * k, torch.float32).view(T, k))
 
 
 def moe_grouped_gemm_w13_swiglu(x, w13, w13_scale, sorted_ids, expert_offsets, k, ws=None, h=None,

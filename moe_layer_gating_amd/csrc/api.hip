@@ -49,10 +49,15 @@ inline bool use_tiles(const moe_shape& s) {
 }
 inline int tiles_bm(const moe_shape& s) { return (long)s.T * s.k < 64L * s.E ? 64 : 128; }
 
-// Few-token launch shortcut of the fused entry point: one block runs gating,
-// grouping, the tile list and the x quantisation up to kRouteSmallMax pairs.
-inline bool route_small(const moe_shape& s) {
-  return !use_tiles(s) && (long)s.T * s.k <= kRouteSmallMax;
+// Grouping kernels by pair count, the same for the fused entry point and for
+// moe_align_sort: one block (gating or given ids, grouping, the tile list, and
+// in the fused FP8 call the x quantisation) up to kRouteSmallMax pairs; one
+// block per expert below kChunkSortMin pairs; the chunked counting sort from
+// there on.
+enum class Grouping { kOneBlock, kPerExpert, kChunked };
+inline Grouping grouping_for(long n_pairs) {
+  if (n_pairs <= kRouteSmallMax) return Grouping::kOneBlock;
+  return n_pairs < kChunkSortMin ? Grouping::kPerExpert : Grouping::kChunked;
 }
 
 Layout layout_for(const moe_shape& s) {
@@ -87,6 +92,33 @@ Layout layout_for(const moe_shape& s) {
   L.max_rtiles = ((long)s.T + kRouterBM - 1) / kRouterBM;
   L.logits = take((size_t)s.T * s.E * 4);
   L.rtiles = take((size_t)(L.max_rtiles + 1) * sizeof(Tile));
+  L.total = o;
+  return L;
+}
+
+// Workspace of moe_align_sort: control words, a tile list of <= kSkinnyBM
+// positions (the one-block and chunked kernels form one) and the chunked
+// sort's scratch.
+struct AlignLayout {
+  size_t ctrl, tiles, chunk_counts, chunk_base, rank, inv, total;
+};
+
+AlignLayout align_layout_for(int T, int k, int E) {
+  AlignLayout L;
+  const long np = (long)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.ctrl = take(sizeof(Ctrl));
+  L.tiles = take((size_t)(max_tiles_for(np, E, kSkinnyBM) + 1) * sizeof(Tile));
+  const size_t n_chunks = (np + kSortChunk - 1) / kSortChunk;
+  L.chunk_counts = take(n_chunks * E * 4);
+  L.chunk_base = take(n_chunks * E * 4);
+  L.rank = take(np * 4);
+  L.inv = take(np >= kChunkSortMin ? np * 4 : 0);
   L.total = o;
   return L;
 }
@@ -143,6 +175,20 @@ size_t moe_workspace_bytes(const moe_shape* s) {
   return layout_for(*s).total;
 }
 
+int moe_workspace_routing(const moe_shape* s, moe_routing_offsets* out) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_for(*s);
+  out->topk_ids = L.ids;
+  out->topk_weights = L.wts;
+  out->expert_counts = L.counts;
+  out->expert_offsets = L.offsets;
+  out->sorted_ids = L.sorted;
+  out->inv_perm = L.inv;
+  return MOE_OK;
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
@@ -168,9 +214,14 @@ int moe_topk_gating(const float* logits, int32_t T, int32_t E, int32_t k, int32_
       launch_topk_gating(logits, T, E, k, renormalize, topk_ids, topk_weights, nullptr, 0, st));
 }
 
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (check_common(T, E, k) != MOE_OK) return 0;
+  return align_layout_for(T, k, E).total;
+}
+
 int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
-                   int32_t* inv_perm, void* stream) {
+                   int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(T, E, k);
   if (rc) return rc;
   if (T == 0) return MOE_OK;
@@ -178,9 +229,35 @@ int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
   if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
       !aligned16(sorted_ids) || (inv_perm && !aligned16(inv_perm)))
     return MOE_ERR_INVALID_ARG;
+  const AlignLayout L = align_layout_for(T, k, E);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || ws_bytes < L.total)
+    return MOE_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return hip_status(launch_align_sort(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_ids,
-                                      inv_perm, st));
+  const long n = (long)T * k;
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  Tile* tiles = at<Tile>(ws, L.tiles);
+  switch (grouping_for(n)) {
+    case Grouping::kOneBlock:
+      // ids are read, not written: the kernel's gating step is skipped
+      return hip_status(launch_route_small(nullptr, T, E, k, 1, const_cast<int32_t*>(topk_ids),
+                                           nullptr, expert_counts, expert_offsets, sorted_ids,
+                                           inv_perm, kSkinnyBM, false, tiles, ctrl, nullptr, 0,
+                                           nullptr, st));
+    case Grouping::kPerExpert:
+      return hip_status(launch_align_sort(topk_ids, T, k, E, expert_counts, expert_offsets,
+                                          sorted_ids, inv_perm, st));
+    case Grouping::kChunked: {
+      // the chunked scatter always writes an inverse permutation; without the
+      // caller's it goes to the workspace
+      int32_t* inv = inv_perm ? inv_perm : at<int32_t>(ws, L.inv);
+      return hip_status(launch_chunk_sort(topk_ids, (int)n, E, expert_counts, expert_offsets,
+                                          sorted_ids, inv, kSkinnyBM, tiles, &ctrl->num_tiles,
+                                          at<int32_t>(ws, L.chunk_counts),
+                                          at<int32_t>(ws, L.chunk_base), at<int32_t>(ws, L.rank),
+                                          st));
+    }
+  }
+  return MOE_ERR_INVALID_ARG;
 }
 
 int moe_grouped_gemm_w13_swiglu(const moe_shape* s, const void* x, const void* w13,
@@ -391,25 +468,25 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   void* h = at<void>(ws, L.h);
   float* y = at<float>(ws, L.y);
 
-  const bool small = route_small(*s);
+  const Grouping grouping = grouping_for((long)T * k);
   uint8_t* xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
   const void* bx = fp8 ? static_cast<const void*>(xq) : x;
 
+  const int bm = big ? tiles_bm(*s) : kSkinnyBM;
+  Tile* tl = big ? tiles_big : tiles;
   MOE_TRY(mark(0));
-  if (small) {
+  if (grouping == Grouping::kOneBlock) {
     MOE_TRY(launch_route_small(logits, T, E, k, s->renormalize, ids, wts, counts, offsets, sorted,
-                               inv, kSkinnyBM, tiles, ctrl, reinterpret_cast<const uint16_t*>(x),
-                               H, xq, st));
+                               inv, bm, big, tl, ctrl, reinterpret_cast<const uint16_t*>(x), H, xq,
+                               st));
     for (int i = 1; i <= 3; i++) MOE_TRY(mark(i));
   } else {
     // zeroes the control block
     MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
                                reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
     MOE_TRY(mark(1));
-    const int bm = big ? tiles_bm(*s) : kSkinnyBM;
-    Tile* tl = big ? tiles_big : tiles;
     int32_t* nt = big ? &ctrl->num_tiles_big : &ctrl->num_tiles;
-    if ((long)T * k >= kChunkSortMin) {
+    if (grouping == Grouping::kChunked) {
       MOE_TRY(launch_chunk_sort(ids, T * k, E, counts, offsets, sorted, inv, bm, tl, nt,
                                 at<int32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.chunk_base),
                                 at<int32_t>(ws, L.rank), st));

@@ -132,11 +132,13 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* c
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
                              hipStream_t st);
 // Gating, grouping, tile list and (xq != nullptr) FP8 quantisation of x in
-// one block, for T*k <= kRouteSmallMax; inv_perm may be null.  Writes every
-// control word.
+// one block, for T*k <= kRouteSmallMax; inv_perm may be null.  With logits ==
+// nullptr the ids are read from `ids` and only the grouping and the tile list
+// are formed.  The tile count goes to ctrl->num_tiles_big when `big`, else to
+// ctrl->num_tiles.  Writes every control word.
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                              int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
+                              int32_t* inv_perm, int bm, bool big, Tile* tiles, Ctrl* ctrl,
                               const uint16_t* x, int H, uint8_t* xq, hipStream_t st);
 // Grouping of n pairs in chunks of kSortChunk plus the tile list of <= bm
 // positions (three launches).  Scratch: chunk_counts and base hold

@@ -55,10 +55,15 @@ __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E,
   const int lane = lane_id();
   float v[kMaxPerLane];
   const int per_lane = (E + kWave - 1) / kWave;
+  // A NaN logit breaks the contract; it is read as -inf so that a violation
+  // still selects experts inside [0, E) (every candidate, -inf included, is
+  // ordered by (value, index)), rather than an index the grouping would use
+  // out of bounds.
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; i++) {
     int e = lane + i * kWave;
-    v[i] = (i < per_lane && e < E) ? row[e] : -INFINITY;
+    const float lv = (i < per_lane && e < E) ? row[e] : -INFINITY;
+    v[i] = (lv == lv) ? lv : -INFINITY;
   }
   uint32_t taken = 0;  // bit i: slot i of this lane already selected (or absent)
 #pragma unroll
@@ -359,7 +364,9 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int* t
 // The whole front of the layer for a small batch (T*k <= kRouteSmallMax
 // pairs) in one block of 16 waves, so that a decode step pays one launch for
 // it instead of one per stage:
-//   1. top-k gating, one wave per token;
+//   1. top-k gating, one wave per token (logits == nullptr: the ids are an
+//      input instead, read from `ids`; the grouping entry point runs steps
+//      2-4 only);
 //   2. expert histogram (LDS integer atomics: counts do not depend on order)
 //      and its exclusive scan -> counts, offsets; thread e owns expert e;
 //   3. the list of tiles of <= bm positions;
@@ -370,11 +377,12 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int* t
 //      block of the same launch, concurrently with steps 1-4 (they share no
 //      data), so the two parts cost the longer of them rather than the sum.
 // Every control word is written here: amax_x (block 1 in FP8 mode, else 0),
-// amax_h = 0 and the tile counts.
+// amax_h = 0 and the tile counts (the list goes to num_tiles_big when `big`,
+// the tiled GEMMs' list, else to num_tiles; the other count is 0).
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ inv_perm, int bm,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ inv_perm, int bm, int big,
     Tile* __restrict__ tiles, Ctrl* ctrl, const uint16_t* __restrict__ x, int H,
     uint8_t* __restrict__ xq) {
   constexpr int NW = 16;
@@ -389,10 +397,14 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   if (blockIdx.x == 0) {  // steps 1-4; in FP8 mode block 1 quantises x
     hist[t] = 0;
 
-    // 1. gating
-    for (int tok = w; tok < T; tok += NW)
-      gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
-                 wts + (size_t)tok * k, s_ids + tok * k, gscr[w]);
+    // 1. gating (or the given ids)
+    if (logits) {
+      for (int tok = w; tok < T; tok += NW)
+        gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
+                   wts + (size_t)tok * k, s_ids + tok * k, gscr[w]);
+    } else if (t < n) {
+      s_ids[t] = ids[t];
+    }
     __syncthreads();
 
     // 2. histogram and scans of the counts and of the tile counts
@@ -439,8 +451,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     if (t == 0) {
       if (!xq) ctrl->amax_x_bits = 0u;
       ctrl->amax_h_bits = 0u;
-      ctrl->num_tiles = total_tiles;
-      ctrl->num_tiles_big = 0;
+      ctrl->num_tiles = big ? 0 : total_tiles;
+      ctrl->num_tiles_big = big ? total_tiles : 0;
     }
   } else {
     // 5. FP8 activation quantisation (x is bf16, H a multiple of 128): four
@@ -502,11 +514,12 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                              int32_t* inv_perm, int bm, Tile* tiles, Ctrl* ctrl,
+                              int32_t* inv_perm, int bm, bool big, Tile* tiles, Ctrl* ctrl,
                               const uint16_t* x, int H, uint8_t* xq, hipStream_t st) {
+  if ((long)T * k > kRouteSmallMax || E > 1024) return hipErrorInvalidValue;
   route_small_kernel<<<xq ? 2 : 1, 1024, 0, st>>>(logits, T, E, k, renorm, ids, w, counts,
-                                                 offsets, sorted_ids, inv_perm, bm, tiles, ctrl,
-                                                 x, H, xq);
+                                                 offsets, sorted_ids, inv_perm, bm, big ? 1 : 0,
+                                                 tiles, ctrl, x, H, xq);
   return hipGetLastError();
 }
 

@@ -90,3 +90,34 @@ def int_tensor(a, dev="cuda"):
 
 def f32_tensor(a, dev="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+
+def fused_call(D, k, mode, renormalize=True, out=None, topk_ids=None, topk_weights=None):
+    """One moe_fused_forward call on an explicit workspace; returns (out,
+    grouping) where grouping holds the counts, offsets, sorted ids and
+    inverse permutation that this very call's kernels wrote into the
+    workspace (NumPy copies), so the grouping the fused path runs can be
+    compared with the oracle bit for bit."""
+    T, H = D["x"].shape
+    E, I2, _ = D["w13"].shape
+    shape = moe.make_shape(T, H, E, k, I2 // 2, mode, renormalize)
+    ws = moe.workspace(shape)
+    ws.fill_(0xA5)  # no stale values can pass for this call's grouping
+    out = moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
+                                D["w2_scale"], k, renormalize=renormalize, out=out, ws=ws,
+                                topk_ids=topk_ids, topk_weights=topk_weights)
+    torch.cuda.synchronize()
+    views = moe.routing_from_workspace(ws, T, E, k)
+    grouping = {n: views[n].cpu().numpy().copy()
+                for n in ("counts", "offsets", "sorted_ids", "inv_perm")}
+    if topk_ids is None:
+        grouping["topk_ids"] = views["topk_ids"].cpu().numpy().copy()
+    return out, grouping
+
+
+def assert_grouping(got, counts, offsets, sorted_ids, inv_perm):
+    """Bit-exact comparison of a grouping with the oracle's."""
+    assert np.array_equal(got["counts"], counts), "expert counts differ"
+    assert np.array_equal(got["offsets"], offsets), "expert offsets differ"
+    assert np.array_equal(got["sorted_ids"], sorted_ids), "sorted ids differ"
+    assert np.array_equal(got["inv_perm"], inv_perm), "inverse permutation differs"

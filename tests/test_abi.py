@@ -70,6 +70,34 @@ def test_check_shape(L, shape, want):
     assert (ws > 0) == (want == 0)
 
 
+def test_align_sort_workspace_bytes(L):
+    assert moe.moe_align_sort_workspace_bytes(4, 2, 8) > 0
+    assert moe.moe_align_sort_workspace_bytes(4, 9, 8) == 0  # k > E
+    assert moe.moe_align_sort_workspace_bytes(-1, 2, 8) == 0
+    small = moe.moe_align_sort_workspace_bytes(1024, 8, 256)   # 8192 pairs: chunked sort
+    big = moe.moe_align_sort_workspace_bytes(4096, 8, 256)
+    assert 0 < small < big and big % 256 == 0
+
+
+def test_workspace_routing_offsets(L):
+    """The routing arrays of a fused call sit inside the workspace, 256-byte
+    aligned, without overlapping one another, and depend only on T, E, k."""
+    for T, E, k in ((1, 64, 8), (8, 8, 2), (4096, 256, 8), (17, 1024, 16)):
+        s = moe.make_shape(T, 7168, E, k, 2048, 2)
+        r = moe.moe_workspace_routing(s)
+        total = moe.moe_workspace_bytes(s)
+        regions = sorted([(r.topk_ids, T * k * 4), (r.topk_weights, T * k * 4),
+                          (r.expert_counts, E * 4), (r.expert_offsets, (E + 1) * 4),
+                          (r.sorted_ids, T * k * 4), (r.inv_perm, T * k * 4)])
+        for (a, n), (b, _) in zip(regions, regions[1:]):
+            assert a % 256 == 0 and a + n <= b
+        assert regions[-1][0] + regions[-1][1] <= total
+        r2 = moe.moe_workspace_routing(moe.make_shape(T, 128, E, k, 128, 0))
+        assert [getattr(r, f) for f, _ in r._fields_] == [getattr(r2, f) for f, _ in r2._fields_]
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_routing(moe.make_shape(4, 100, 8, 2, 256, 0))
+
+
 def test_workspace_grows_with_tokens(L):
     a = moe.moe_workspace_bytes(moe.make_shape(1, 4096, 64, 8, 8192, 2))
     b = moe.moe_workspace_bytes(moe.make_shape(16, 4096, 64, 8, 8192, 2))
@@ -90,10 +118,16 @@ def test_invalid_pointers_rejected_before_launch(L):
     assert L.moe_topk_gating(good, 4, 8, 9, 1, good, good, None) == -1
     assert L.moe_topk_gating(good, 4, 8, 2, 2, good, good, None) == -1
     assert L.moe_topk_gating(good, 0, 8, 2, 1, good, good, None) == 0  # T = 0: nothing enqueued
-    # align sort
-    assert L.moe_align_sort(good, 4, 2, 8, None, good, good, None, None) == -1
-    assert L.moe_align_sort(good, 4, 2, 8, good, good, odd, None, None) == -1
-    assert L.moe_align_sort(good, 0, 2, 8, good, good, good, None, None) == 0
+    # align sort: pointers, then the workspace (missing, misaligned, small)
+    aws = moe.moe_align_sort_workspace_bytes(4, 2, 8)
+    wsa = _fake(0x300000)
+    assert L.moe_align_sort(good, 4, 2, 8, None, good, good, None, wsa, aws, None) == -1
+    assert L.moe_align_sort(good, 4, 2, 8, good, good, odd, None, wsa, aws, None) == -1
+    assert L.moe_align_sort(good, 4, 2, 8, good, good, good, None, None, aws, None) == -3
+    assert L.moe_align_sort(good, 4, 2, 8, good, good, good, None, _fake(0x300010), aws,
+                            None) == -3
+    assert L.moe_align_sort(good, 4, 2, 8, good, good, good, None, wsa, aws - 1, None) == -3
+    assert L.moe_align_sort(good, 0, 2, 8, good, good, good, None, None, 0, None) == 0
     s = moe.make_shape(4, 256, 8, 2, 256, 2)
     S = ctypes.byref(s)
     need = moe.moe_workspace_bytes(s)

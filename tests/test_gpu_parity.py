@@ -25,8 +25,9 @@ import torch
 import moe_layer_gating_amd as moe
 import moe_workloads as wl
 import oracle
-from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, bf16_step_ratio,
-                         f32_tensor, int_tensor, rel_inf, say, upload)
+from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, assert_grouping,
+                         bf16_step_ratio, f32_tensor, fused_call, int_tensor, rel_inf, say,
+                         upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,10 +191,12 @@ def test_fused_forward(c):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     say("fused", c[0])
-    moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"], D["w2_scale"], k,
-                          out=out, topk_ids=ids, topk_weights=w)
-    torch.cuda.synchronize()
+    _, grp = fused_call(D, k, mode, out=out, topk_ids=ids, topk_weights=w)
     assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
+    assert np.max(np.abs(w.cpu().numpy() - ref["topk_weights"])) <= 1e-6
+    # the grouping this call's own kernels wrote (one-block front, one block
+    # per expert, or the chunked sort, by pair count)
+    assert_grouping(grp, ref["counts"], ref["offsets"], ref["sorted_ids"], ref["inv_perm"])
     og = oracle.to_f64(act_to_numpy(out, mode), mode)
     assert not np.isnan(og).any()  # every row written
     # reference: the oracle's output before its rounding to the output type
@@ -249,10 +252,12 @@ def test_gating_ties_and_neginf():
 
 @pytest.mark.parametrize("E,k,T", [(64, 8, 32), (128, 8, 16), (100, 6, 20), (5, 5, 3), (8, 2, 16)])
 def test_fused_front_gating_ties_and_neginf(E, k, T):
-    """The fused entry point's one-block front kernel (T*k <= 256, few pairs
-    per expert) selects by ranks for E <= 128: ids bit-exact and weights within
-    1e-6 of the oracle on tie-heavy, -inf and signed-zero logits, with both
-    weight rules, and the grouping it writes matches the oracle's."""
+    """The fused entry point's one-block front kernel (T*k <= 256) selects by
+    ranks for E <= 128: ids bit-exact and weights within 1e-6 of the oracle on
+    tie-heavy, -inf and signed-zero logits, with both weight rules; the
+    grouping the same kernel writes into the workspace (counts, offsets,
+    sorted ids, inverse permutation) is bit-exact against the oracle's
+    grouping of those ids."""
     rng = np.random.default_rng(E * 100 + k)
     L = wl.make_layer(wl.scaled("front_%d_%d" % (E, k), T, 128, E, k, 128, BF16, seed=E + k))
     D = upload(L)
@@ -269,12 +274,12 @@ def test_fused_front_gating_ties_and_neginf(E, k, T):
             say("fused front gating E=%d k=%d kind=%d renorm=%d" % (E, k, kind, renorm))
             ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
             w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-            moe.moe_fused_forward(D["x"], torch.from_numpy(l).cuda(), D["w13"], None, D["w2"],
-                                  None, k, renormalize=renorm, topk_ids=ids, topk_weights=w)
-            torch.cuda.synchronize()
+            Dl = dict(D, logits=torch.from_numpy(l).cuda())
+            _, grp = fused_call(Dl, k, BF16, renormalize=renorm, topk_ids=ids, topk_weights=w)
             rid, rw = oracle.topk_gating(l, k, renorm)
             assert np.array_equal(ids.cpu().numpy(), rid)
             assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+            assert_grouping(grp, *oracle.align_sort(rid, E))
 
 
 def _act_quant_case(bits):
@@ -335,6 +340,56 @@ def test_align_sort_large_skewed():
     assert np.array_equal(inv.cpu().numpy(), ri)
 
 
+@pytest.mark.parametrize("T,k,E", [(32, 8, 64), (128, 2, 1024), (257, 1, 8), (300, 8, 64),
+                                   (1023, 8, 256), (1024, 8, 256), (4097, 2, 1024),
+                                   (700, 16, 33)])
+def test_align_sort_every_grouping_kernel(T, k, E):
+    """moe_align_sort at and around the pair counts where the grouping kernel
+    changes (256 pairs: one block; below 8192: one block per expert; 8192
+    and more: the chunked counting sort), with uniform and Zipf-skewed ids;
+    every output bit-exact, and inv_perm may be omitted."""
+    rng = np.random.default_rng(T * 31 + E)
+    for skew in (False, True):
+        p = 1.0 / np.arange(1, E + 1) ** 1.1 if skew else np.ones(E)
+        p = p / p.sum()
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+        ids = ids.astype(np.int32)
+        say("align_sort T=%d k=%d E=%d skew=%d (%d pairs)" % (T, k, E, skew, T * k))
+        counts, offsets, sorted_ids, inv = moe.moe_align_sort(int_tensor(ids), E)
+        c2, o2, s2, _ = moe.moe_align_sort(int_tensor(ids), E, with_inv=False)
+        torch.cuda.synchronize()
+        rc, ro, rs, ri = oracle.align_sort(ids, E)
+        got = dict(counts=counts.cpu().numpy(), offsets=offsets.cpu().numpy(),
+                   sorted_ids=sorted_ids.cpu().numpy(), inv_perm=inv.cpu().numpy())
+        assert_grouping(got, rc, ro, rs, ri)
+        assert np.array_equal(c2.cpu().numpy(), rc) and np.array_equal(o2.cpu().numpy(), ro)
+        assert np.array_equal(s2.cpu().numpy(), rs)
+
+
+def test_gating_nan_logits_stay_in_range():
+    """NaN logits break the contract; both gating kernels read them as -inf,
+    so the ids stay inside [0, E) (and equal the oracle's ids on the logits
+    with NaN replaced by -inf) and the fused call's grouping stays in range."""
+    rng = np.random.default_rng(11)
+    T, E, k = 24, 64, 8
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[rng.random((T, E)) < 0.3] = np.nan
+    l[3, :] = np.nan  # a row of NaN only
+    l[4, : E - 2] = np.nan  # fewer than k non-NaN entries
+    clean = np.where(np.isnan(l), np.float32(-np.inf), l)
+    rid, _ = oracle.topk_gating(clean, k)
+    say("gating NaN logits")
+    ids, _ = moe.moe_topk_gating(torch.from_numpy(l).cuda(), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    L = wl.make_layer(wl.scaled("nan_front", T, 128, E, k, 128, BF16, seed=3))
+    D = dict(upload(L), logits=torch.from_numpy(l).cuda())
+    ids2 = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    _, grp = fused_call(D, k, BF16, topk_ids=ids2)
+    assert np.array_equal(ids2.cpu().numpy(), rid)
+    assert_grouping(grp, *oracle.align_sort(rid, E))
+
+
 # Planted routing: expert counts on both sides of the tile boundaries and of
 # the quarter / half / full main-loop widths (0, 1, 15-17, 31-33, 63-65, 96,
 # 127-129, 255-257, 540, ...), so experts get exact, ragged and single-row
@@ -362,9 +417,9 @@ def test_planted_tile_edges(c):
     assert np.array_equal(ref["counts"], np.array(counts, np.int32))
     D = upload(L)
     say("planted fused", name)
-    out = moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"],
-                                D["w2_scale"], k)
-    torch.cuda.synchronize()
+    out, grp = fused_call(D, k, mode)
+    assert np.array_equal(grp["topk_ids"], ref["topk_ids"])
+    assert_grouping(grp, ref["counts"], ref["offsets"], ref["sorted_ids"], ref["inv_perm"])
     og = oracle.to_f64(act_to_numpy(out, mode), mode)
     assert not np.isnan(og).any()
     err = rel_inf(og, ref["out_exact"])
@@ -468,10 +523,9 @@ def test_random_shape_sweep(c):
     out = torch.full((T, H), float("nan"), dtype=moe.act_dtype(mode), device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     say("random shape", c)
-    moe.moe_fused_forward(D["x"], D["logits"], D["w13"], D["w13_scale"], D["w2"], D["w2_scale"], k,
-                          out=out, topk_ids=ids)
-    torch.cuda.synchronize()
+    _, grp = fused_call(D, k, mode, out=out, topk_ids=ids)
     assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
+    assert_grouping(grp, ref["counts"], ref["offsets"], ref["sorted_ids"], ref["inv_perm"])
     og = oracle.to_f64(act_to_numpy(out, mode), mode)
     assert not np.isnan(og).any()
     err = rel_inf(og, ref["out_exact"])

@@ -186,3 +186,59 @@ def test_out_is_the_rounding_of_out_exact(mode):
     else:
         assert np.array_equal(r["out"].ravel(), bf.f64_to_bf16_values(r["out_exact"]).astype(
             np.float32).view(np.uint32).ravel().__rshift__(16).astype(np.uint16))
+
+
+def _ulp(v, mode):
+    """Spacing of the output type at |v| (fp32, or bf16 in the other modes)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.exp2(e - (23 if mode == F32 else 7))
+
+
+@pytest.mark.parametrize("mode", [F32, BF16])
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (7, 3, 5), (33, 8, 64), (16, 16, 16)])
+def test_combine_f32_pins(mode, T, k, E):
+    """oracle_combine_f32 (the expected value of the GPU combine stage test),
+    pinned three ways on fp32 y in sorted order:
+      * the double-precision oracle_combine on the same y widened to double
+        (exact widening: identical sums, identical results);
+      * a dense mixing matrix M[t, inv_perm[t*k+j]] = w[t,j] applied with a
+        float64 matmul (a different construction: a wrong index, a swapped
+        weight or a dropped slot changes it by far more than the one output
+        ulp that the summation order may move);
+      * special cases: k = 1 with weight 1 is an exact gather of y's rows;
+        equal weights on equal rows return that row."""
+    rng = np.random.default_rng(T * 100 + k * 10 + E)
+    H = 24
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, sorted_ids, inv = oracle.align_sort(ids, E)
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    got = oracle.to_f64(oracle.combine(mode, y, inv, w), mode)
+    want_dd = oracle.to_f64(oracle.combine(mode, y.astype(np.float64), inv, w), mode)
+    assert np.array_equal(got, want_dd)
+    M = np.zeros((T, T * k))
+    for t in range(T):
+        for j in range(k):
+            M[t, inv[t * k + j]] += w[t, j]
+    dense = M @ y.astype(np.float64)
+    assert np.all(np.abs(got - dense) <= _ulp(dense, mode))
+    # k = 1, weight 1: out is y gathered by inv_perm, exactly (bf16: rounded once)
+    if k == 1:
+        g1 = oracle.to_f64(oracle.combine(mode, y, inv, np.ones((T, 1), np.float32)), mode)
+        gather = y.astype(np.float64)[inv]
+        if mode == F32:
+            assert np.array_equal(g1, gather)
+        else:
+            assert np.array_equal(g1, oracle.to_f64(oracle.bf16_round(gather), BF16).reshape(T, H))
+    # equal weights on equal rows: the row itself
+    row = rng.standard_normal(H).astype(np.float32)
+    ysame = np.tile(row, (T * k, 1))
+    wq = np.full((T, k), np.float32(1.0 / k), np.float32) if k in (1, 2, 8, 16) else None
+    if wq is not None:  # 1/k exact in fp32, sums of k equal terms exact
+        g2 = oracle.to_f64(oracle.combine(mode, ysame, inv, wq), mode)
+        r = row.astype(np.float64)[None, :].repeat(T, 0)
+        if mode == F32:
+            assert np.array_equal(g2, r)
+        else:
+            assert np.array_equal(g2, oracle.to_f64(oracle.bf16_round(r), BF16).reshape(T, H))
