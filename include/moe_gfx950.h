@@ -65,7 +65,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad T, E, k, dtype */
   MOE_ERR_UNSUPPORTED = -2, /* H or I not a multiple of 128 */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  MOE_ERR_HIP = -4          /* a kernel launch failed */
+  MOE_ERR_HIP = -4,         /* a kernel launch failed */
+  MOE_ERR_TOO_LARGE = -5    /* beyond moe_fused_forward_noalloc's scratch */
 } moe_status;
 
 /* Layer shape (host struct).  renormalize: 1 = top-k softmax renormalised
@@ -239,6 +240,23 @@ int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, co
                       const float* w13_scale, const void* w2, const float* w2_scale, void* out,
                       int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_fused_forward, same kernels and same results, without a
+ * workspace argument.  Its scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its first
+ * use on that GPU until the process ends; nothing is allocated or freed per
+ * call.  Shapes whose moe_workspace_bytes exceeds that size return
+ * MOE_ERR_TOO_LARGE with nothing enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  Arguments and errors otherwise as moe_fused_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_fused_forward_noalloc(const moe_shape* s, const void* x, const float* logits,
+                              const void* w13, const float* w13_scale, const void* w2,
+                              const float* w2_scale, void* out, int32_t* topk_ids,
+                              float* topk_weights, void* stream);
 
 /* Router GEMM: logits[t][e] = sum_h x[t][h] * wg[e][h] with fp32
  * accumulation, for the top-k gating (readmex.ai, "AWS details fused MoE

@@ -44,7 +44,8 @@ EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string",
            "moe_align_sort", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_w2", "moe_combine",
            "moe_act_quant_e4m3",
            "moe_fused_forward", "moe_fused_forward_events", "moe_router_logits",
-           "moe_fused_forward_router")
+           "moe_fused_forward_router", "moe_fused_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 # host-only calls whose return type is not a moe_status
 _NON_STATUS = ("moe_workspace_bytes", "moe_status_string", "moe_align_sort_workspace_bytes")
 NUM_STAGE_EVENTS = 9
@@ -76,6 +77,7 @@ def lib():
         L.moe_combine.argtypes = [S, P, P, P, P, P]
         L.moe_act_quant_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
         L.moe_fused_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_fused_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
         L.moe_router_logits.argtypes = [S, P, P, P, P, sz, P]
         L.moe_fused_forward_router.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_fused_forward_events.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P,
@@ -273,6 +275,21 @@ def moe_fused_forward(x, logits, w13, w13_scale, w2, w2_scale, k, renormalize=Tr
                                    _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
                                    _ptr(topk_ids), _ptr(topk_weights), _ptr(ws), ws.numel(),
                                    _stream()), "moe_fused_forward")
+    return out
+
+
+def moe_fused_forward_noalloc(x, logits, w13, w13_scale, w2, w2_scale, k, out,
+                              renormalize=True, topk_ids=None, topk_weights=None):
+    """moe_fused_forward on the library's static scratch: no workspace, and
+    the caller passes `out` (nothing is allocated here either)."""
+    mode = mode_of(w13)
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    shape = make_shape(T, H, E, k, I2 // 2, mode, renormalize)
+    _check(lib().moe_fused_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w13),
+                                           _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(out),
+                                           _ptr(topk_ids), _ptr(topk_weights), _stream()),
+           "moe_fused_forward_noalloc")
     return out
 
 

@@ -10,10 +10,17 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "moe_common.h"
 
 using namespace moe;
+
+// Scratch of moe_fused_forward_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it only names the symbol); it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -196,6 +203,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape (H and I must be multiples of 128)";
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "HIP launch failure";
+    case MOE_ERR_TOO_LARGE:
+      return "shape needs more scratch than moe_fused_forward_noalloc's static buffer";
     default: return "unknown status";
   }
 }
@@ -562,6 +571,40 @@ int moe_fused_forward(const moe_shape* s, const void* x, const float* logits, co
                       void* stream) {
   return fused_impl(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
                     ws_bytes, stream, nullptr);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+static void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  static bool done[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+    done[dev] = true;
+  }
+  return ptr[dev];
+}
+
+int moe_fused_forward_noalloc(const moe_shape* s, const void* x, const float* logits,
+                              const void* w13, const float* w13_scale, const void* w2,
+                              const float* w2_scale, void* out, int32_t* topk_ids,
+                              float* topk_weights, void* stream) {
+  int rc = moe_check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (moe_workspace_bytes(s) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  // the kernels clear what must start at zero (the control words) themselves
+  return fused_impl(s, x, logits, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
+                    (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_fused_forward_events(const moe_shape* s, const void* x, const float* logits,

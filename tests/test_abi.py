@@ -152,6 +152,22 @@ def test_invalid_pointers_rejected_before_launch(L):
                                None, ws, moe.moe_workspace_bytes(s0), None) == 0
 
 
+def test_noalloc_rejects_shapes_beyond_its_scratch(L):
+    # the prefill layer needs about 1.2 GB of scratch: refused before any
+    # pointer is looked at or anything is enqueued
+    s = moe.make_shape(4096, 7168, 256, 8, 2048, 2)
+    assert moe.moe_workspace_bytes(s) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_fused_forward_noalloc(ctypes.byref(s), None, None, None, None, None, None, None,
+                                       None, None, None) == -5
+    assert L.moe_status_string(-5)
+    s0 = moe.make_shape(0, 7168, 256, 8, 2048, 2)
+    assert L.moe_fused_forward_noalloc(ctypes.byref(s0), None, None, None, None, None, None, None,
+                                       None, None, None) == 0
+    bad = moe.make_shape(4, 100, 8, 2, 256, 2)
+    assert L.moe_fused_forward_noalloc(ctypes.byref(bad), None, None, None, None, None, None,
+                                       None, None, None, None) == -2
+
+
 def test_act_quant_rejects_before_launch(L):
     good = _fake(0x100000)
     odd = _fake(0x100004)
