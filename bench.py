@@ -25,8 +25,10 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   bf16 MFMA, 2.5 PFLOP/s), a secondary figure;
   roofline     -- the dominant kernel (the gate/up GEMM): its algorithmic
                   bytes (or flops) per launch / its average duration, timed
-                  with HIP events recorded on the launch stream around that
-                  kernel in every timed step, against 8 TB/s (or the MFMA
+                  with HIP events taken by that kernel's own dispatch in
+                  each of K further steps right after the timed ones
+                  (ms_per_step_kernel_timed is their wall time per step),
+                  against 8 TB/s (or the MFMA
                   peak of the layer's type when its arithmetic intensity is
                   above that ridge); `traffic` = its HBM bytes per launch from
                   rocprofv3 FETCH_SIZE / WRITE_SIZE counters
@@ -42,8 +44,10 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   reading a 1 GiB buffer that evicts L2 and the 256 MB MALL:
                   median, p10 and p90, as a separate figure;
   router       -- the layer run from the router weights instead of the logits
-                  (moe_fused_forward_router), per step, and the router GEMM
-                  alone, as separate figures;
+                  (moe_fused_forward_router: for few-token bf16/FP8 batches
+                  the front kernel computes the logits itself, one launch
+                  fewer), per step, and the router GEMM alone, as separate
+                  figures (also in each sub-record);
   sub_records  -- the same step figures for the sub-record layers.
 """
 from __future__ import annotations
@@ -252,17 +256,25 @@ def measure(name, args, H_, full):
     torch.cuda.synchronize()
     counts = np.bincount(lay.ids.cpu().numpy().ravel(), minlength=spec.E)
 
-    # timed region: every step records an event pair around the gate/up GEMM
-    # (stage boundaries 4 and 5) on the stream the kernels run on
-    pairs = [(new_event(), new_event()) for _ in range(args.steps)]
+    # timed region: K plain steps (moe_fused_forward, as a caller runs it)
     log("%s: timing %d steps" % (name, args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lay.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the dominant kernel's duration: K more steps, each taking the gate/up
+    # GEMM dispatch's own start / end time (stage boundaries 4 and 5, on the
+    # stream the kernels run on); that instrumentation adds host work per
+    # step, so these steps are not the ones `value` comes from
+    pairs = [(new_event(), new_event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in pairs:
         lay.step([None, None, None, None, a, b, None, None, None])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed * 1e3 / args.steps
+    ev_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     w13_ms = float(np.mean([elapsed_ms(a, b) for a, b in pairs]))
     own_events = [e for p in pairs for e in p]
 
@@ -290,6 +302,7 @@ def measure(name, args, H_, full):
                                                      spec.I),
         "dtype": DTYPE_NAME[mode],
         "ms_per_step": ms,
+        "ms_per_step_kernel_timed": ev_ms,
         "tokens_per_s": spec.T / (ms * 1e-3),
         "active_experts": active,
         "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
@@ -301,6 +314,36 @@ def measure(name, args, H_, full):
         "layer_alg_flops": flops,
         "roofline": roofline,
     }
+    # the layer from the router weights (a separate figure): the same steps
+    # from x and the router weights (moe_fused_forward_router: for few-token
+    # bf16/FP8 batches the front kernel computes the logits itself), and the
+    # router GEMM alone (moe_router_logits)
+    lg = torch.empty((spec.T, spec.E), dtype=torch.float32, device="cuda")
+
+    def router_step():
+        moe.moe_fused_forward_router(lay.x, lay.wg, lay.w13, lay.s13, lay.w2, lay.s2, spec.k,
+                                     out=lay.out, ws=lay.ws, topk_ids=lay.ids)
+
+    for _ in range(args.warmup):
+        router_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        router_step()
+    torch.cuda.synchronize()
+    router_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ra, rb = new_event(), new_event()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    H_.hipEventRecord(ctypes.c_void_p(ra), stream)
+    for _ in range(args.steps):
+        moe.moe_router_logits(lay.x, lay.wg, k=spec.k, ws=lay.ws, logits=lg)
+    H_.hipEventRecord(ctypes.c_void_p(rb), stream)
+    torch.cuda.synchronize()
+    router_ms = elapsed_ms(ra, rb) / args.steps
+    own_events += [ra, rb]
+    rec["router"] = {"ms_per_step": router_step_ms,
+                     "tokens_per_s": spec.T / (router_step_ms * 1e-3),
+                     "router_gemm_ms": router_ms}
     if full:
         # the same step replayed from a captured HIP graph (a separate,
         # labelled figure: launches without per-launch CPU work; `value`
@@ -317,31 +360,6 @@ def measure(name, args, H_, full):
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         del graph
-
-        # the layer from the router weights (a separate figure): the same
-        # steps with the router in front, and the router GEMM alone
-        lg = torch.empty((spec.T, spec.E), dtype=torch.float32, device="cuda")
-
-        def router_step():
-            moe.moe_fused_forward_router(lay.x, lay.wg, lay.w13, lay.s13, lay.w2, lay.s2, spec.k,
-                                         out=lay.out, ws=lay.ws, logits=lg)
-
-        for _ in range(args.warmup):
-            router_step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            router_step()
-        torch.cuda.synchronize()
-        router_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        ra, rb = new_event(), new_event()
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        H_.hipEventRecord(ctypes.c_void_p(ra), stream)
-        for _ in range(args.steps):
-            moe.moe_router_logits(lay.x, lay.wg, k=spec.k, ws=lay.ws, logits=lg)
-        H_.hipEventRecord(ctypes.c_void_p(rb), stream)
-        torch.cuda.synchronize()
-        router_ms = elapsed_ms(ra, rb) / args.steps
 
         # single calls after an L2 / MALL flush (outside the timed region):
         # the flush only reads, so the timed call inherits no dirty lines
@@ -363,14 +381,11 @@ def measure(name, args, H_, full):
             H_.hipEventSynchronize(ctypes.c_void_p(evs[-1]))
             stage_ms += [elapsed_ms(evs[i], evs[i + 1]) for i in range(moe.NUM_STAGE_EVENTS - 1)]
         stage_ms /= reps
-        own_events += evs + [ra, rb] + [e for p in fpairs for e in p]
+        own_events += evs + [e for p in fpairs for e in p]
         rec.update({
             "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": spec.T / (graph_ms * 1e-3),
                              "layer_hbm_frac": layer_bytes / (graph_ms * 1e-3) / 1e9 /
                              HBM_PEAK_GBS},
-            "router": {"ms_per_step": router_step_ms,
-                       "tokens_per_s": spec.T / (router_step_ms * 1e-3),
-                       "router_gemm_ms": router_ms},
             "flushed": {"calls": len(fms), "ms_median": float(np.median(fms)),
                         "ms_p10": float(np.percentile(fms, 10)),
                         "ms_p90": float(np.percentile(fms, 90)),

@@ -251,7 +251,7 @@ int moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
       return hip_status(launch_route_small(nullptr, T, E, k, 1, const_cast<int32_t*>(topk_ids),
                                            nullptr, expert_counts, expert_offsets, sorted_ids,
                                            inv_perm, kSkinnyBM, false, tiles, ctrl, nullptr, 0,
-                                           nullptr, st));
+                                           nullptr, nullptr, nullptr, st));
     case Grouping::kPerExpert:
       return hip_status(launch_align_sort(topk_ids, T, k, E, expert_counts, expert_offsets,
                                           sorted_ids, inv_perm, st));
@@ -442,10 +442,21 @@ int check_fused_args(const moe_shape* s, const void* x, const float* logits, con
   return check_ws(s, ws, ws_bytes);
 }
 
+// Router fused into the front kernel: bf16 router weights (BF16 and FP8
+// layers) small enough for one block to stream, a batch the one-block front
+// takes, and logits that fit its LDS.
+inline bool router_in_front(const moe_shape& s) {
+  return s.wdtype != MOE_F32 && grouping_for((long)s.T * s.k) == Grouping::kOneBlock &&
+         (long)s.T * s.E <= kFusedRouterMaxTE && (long)s.E * s.H <= kFusedRouterMaxEH;
+}
+
+// The layer.  With wg (only when router_in_front), the front kernel computes
+// the logits from x and wg itself and copies them to logits_out if given;
+// `logits` is then unused.
 int fused_impl(const moe_shape* s, const void* x, const float* logits, const void* w13,
                const float* w13_scale, const void* w2, const float* w2_scale, void* out,
                int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream,
-               void** events) {
+               void** events, const void* wg = nullptr, float* logits_out = nullptr) {
   int rc = moe_check_shape(s);
   if (rc) return rc;
   if (s->T == 0) return MOE_OK;
@@ -485,9 +496,10 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   Tile* tl = big ? tiles_big : tiles;
   MOE_TRY(mark(0));
   if (grouping == Grouping::kOneBlock) {
-    MOE_TRY(launch_route_small(logits, T, E, k, s->renormalize, ids, wts, counts, offsets, sorted,
-                               inv, bm, big, tl, ctrl, reinterpret_cast<const uint16_t*>(x), H, xq,
-                               st));
+    MOE_TRY(launch_route_small(wg ? nullptr : logits, T, E, k, s->renormalize, ids, wts, counts,
+                               offsets, sorted, inv, bm, big, tl, ctrl,
+                               reinterpret_cast<const uint16_t*>(x), H, xq,
+                               reinterpret_cast<const uint16_t*>(wg), logits_out, st));
     for (int i = 1; i <= 3; i++) MOE_TRY(mark(i));
   } else {
     // zeroes the control block
@@ -556,10 +568,15 @@ int moe_fused_forward_router(const moe_shape* s, const void* x, const void* wg, 
   if ((rc = check_router_args(s, x, wg, logits))) return rc;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   float* lg = logits ? logits : at<float>(ws, layout_for(*s).logits);
-  // every argument of the layer is checked before the router is enqueued
+  // every argument of the layer is checked before anything is enqueued
   if ((rc = check_fused_args(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids,
                              topk_weights, ws, ws_bytes)))
     return rc;
+  // few-token batches: one front kernel computes the logits, gates and
+  // groups (no router launch, the logits stay on chip)
+  if (router_in_front(*s))
+    return fused_impl(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
+                      ws_bytes, stream, nullptr, wg, logits);
   if ((rc = router_impl(s, x, wg, lg, ws, reinterpret_cast<hipStream_t>(stream)))) return rc;
   return fused_impl(s, x, lg, w13, w13_scale, w2, w2_scale, out, topk_ids, topk_weights, ws,
                     ws_bytes, stream, nullptr);

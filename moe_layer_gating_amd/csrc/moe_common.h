@@ -17,6 +17,12 @@ constexpr int kSortChunk = 1024;     // pairs per chunk of the many-pair groupin
 constexpr int kChunkSortMin = 8192;  // pairs from which the chunked grouping is used
 constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)
 constexpr int kRouterBM = 64;    // tokens per tile of the tiled router GEMM
+constexpr int kFusedRouterMaxTE = 4096;  // logits the front kernel keeps in LDS (T * E)
+// router weights (E * H bf16 values) the front kernel reads itself: one CU
+// streams them, so beyond this a separate many-block router launch is faster
+// (measured: E = 64, H = 4096 cost 15 us in one block against 10 us for the
+// separate launch)
+constexpr long kFusedRouterMaxEH = 131072;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -132,14 +138,18 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* c
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
                              hipStream_t st);
 // Gating, grouping, tile list and (xq != nullptr) FP8 quantisation of x in
-// one block, for T*k <= kRouteSmallMax; inv_perm may be null.  With logits ==
-// nullptr the ids are read from `ids` and only the grouping and the tile list
-// are formed.  The tile count goes to ctrl->num_tiles_big when `big`, else to
-// ctrl->num_tiles.  Writes every control word.
+// one block, for T*k <= kRouteSmallMax; inv_perm may be null.  With wg (bf16
+// router weights [E,H], T*E <= kFusedRouterMaxTE) the logits are computed in
+// the kernel from x and wg (and copied to logits_out if that is given);
+// otherwise they are read from `logits`.  With neither, the ids are read from
+// `ids` and only the grouping and the tile list are formed.  The tile count
+// goes to ctrl->num_tiles_big when `big`, else to ctrl->num_tiles.  Writes
+// every control word.
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                               int32_t* inv_perm, int bm, bool big, Tile* tiles, Ctrl* ctrl,
-                              const uint16_t* x, int H, uint8_t* xq, hipStream_t st);
+                              const uint16_t* x, int H, uint8_t* xq, const uint16_t* wg,
+                              float* logits_out, hipStream_t st);
 // Grouping of n pairs in chunks of kSortChunk plus the tile list of <= bm
 // positions (three launches).  Scratch: chunk_counts and base hold
 // ceil(n / kSortChunk) * E ints each, rank n ints.

@@ -336,6 +336,108 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------ router inside the front
+// The router GEMM of a small batch, computed by the front kernel itself so
+// that the gating reads the logits from LDS: no router launch in front and no
+// logits round trip through HBM (token routing as the first stage of the one
+// fused operation: readmex.ai, "AWS details fused MoE kernel optimizations on
+// SageMaker, up to 10% throughput gain", summary; routing logic kept inside
+// the fused kernels rather than in separate steps: explore.n1n.ai,
+// "Mixture-of-Experts Kernel Engineering on Amazon SageMaker AI", section
+// "2. Triton Backend Routing for FP8 Quantization").
+//
+// lgs[t * E + e] = x[t] . wg[e] for t < T, e < E (x [T,H], wg [E,H] bf16).
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16): experts on the row side, tokens on
+// the column side, 16 x 16 output tiles; exact products, fp32 sums.  A work
+// item is up to 4 expert tiles of one token tile (the token fragment loaded
+// once for all 4) over a range of K.  With few items the 16 waves split K
+// into `parts` ranges and the partial tiles are added through LDS in range
+// order, one expert tile at a time; otherwise each wave takes whole items.
+// Every lane loads 16 bytes (8 values) of K per step from one row of each
+// operand, at the same K offsets on both sides.
+__device__ __forceinline__ void router_logits_block(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ wg, int T, int H,
+                                                    int E, float* lgs, float (*part)[256]) {
+  constexpr int NW = 16, U = 2;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int n_et = (E + 15) / 16, n_tt = (T + 15) / 16;
+  const int n_eg = (n_et + 3) / 4, n_groups = n_eg * n_tt;
+  const int n_steps = H / 32;
+  int parts = NW / n_groups;
+  parts = parts < 1 ? 1 : (parts > n_steps ? n_steps : parts);
+  const i32x4 z4 = {0, 0, 0, 0};
+  for (int base = 0; base < n_groups * parts; base += NW) {  // uniform over the block
+    const int item = base + w;
+    const bool live = item < n_groups * parts;
+    const int grp = live ? item / parts : 0, p = live ? item - grp * parts : 0;
+    const int eg = grp % n_eg, tt = grp / n_eg;
+    const int t = tt * 16 + r;
+    const bool vt = live && t < T;
+    const char* brow = reinterpret_cast<const char*>(x + (size_t)(vt ? t : 0) * H) + g * 16;
+    const char* arow[4];
+    bool ve[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int e = (eg * 4 + q) * 16 + r;
+      ve[q] = live && e < E;
+      arow[q] = reinterpret_cast<const char*>(wg + (size_t)(ve[q] ? e : 0) * H) + g * 16;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int s0 = live ? (int)((long)p * n_steps / parts) : 0;
+    const int s1 = live ? (int)((long)(p + 1) * n_steps / parts) : 0;
+    for (int s = s0; s < s1; s += U) {
+      i32x4 a[U][4], b[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const bool in = s + u < s1;
+        const size_t off = (size_t)(s + u) * 64;
+        b[u] = (in && vt) ? *reinterpret_cast<const i32x4*>(brow + off) : z4;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          a[u][q] = (in && ve[q]) ? *reinterpret_cast<const i32x4*>(arow[q] + off) : z4;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][q]),
+                                                           __builtin_bit_cast(bf16x8, b[u]),
+                                                           acc[q], 0, 0, 0);
+    }
+    // lane (r, g) holds rows 4g .. 4g+3 (experts) of column r (token)
+    if (parts == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int e = (eg * 4 + q) * 16 + 4 * g + i;
+          if (vt && e < E) lgs[t * E + e] = acc[q][i];
+        }
+    } else {  // a single round: add the parts of each expert tile in order
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if (live) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) part[w][lane * 4 + i] = acc[q][i];
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < n_groups * 256; idx += blockDim.x) {
+          const int gi = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
+          float sum = 0.f;
+          for (int pp = 0; pp < parts; pp++) sum += part[gi * parts + pp][l * 4 + i];
+          const int e = ((gi % n_eg) * 4 + q) * 16 + 4 * (l >> 4) + i;
+          const int tk = (gi / n_eg) * 16 + (l & 15);
+          if (tk < T && e < E) lgs[tk * E + e] = sum;
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------- small batches
 // Exclusive scan of one int per thread over a 1024-thread block; returns the
 // prefix and writes the block total to *total.  `tmp` holds 16 ints of LDS.
@@ -364,9 +466,13 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int* t
 // The whole front of the layer for a small batch (T*k <= kRouteSmallMax
 // pairs) in one block of 16 waves, so that a decode step pays one launch for
 // it instead of one per stage:
-//   1. top-k gating, one wave per token (logits == nullptr: the ids are an
-//      input instead, read from `ids`; the grouping entry point runs steps
-//      2-4 only);
+//   0. with router weights wg (bf16, T * E <= kFusedRouterMaxTE, E * H <=
+//      kFusedRouterMaxEH): the
+//      router GEMM into LDS (router_logits_block), copied to logits_out if
+//      given; the gating then reads the LDS copy;
+//   1. top-k gating, one wave per token (logits == nullptr and wg ==
+//      nullptr: the ids are an input instead, read from `ids`; the grouping
+//      entry point runs steps 2-4 only);
 //   2. expert histogram (LDS integer atomics: counts do not depend on order)
 //      and its exclusive scan -> counts, offsets; thread e owns expert e;
 //   3. the list of tiles of <= bm positions;
@@ -384,9 +490,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     float* __restrict__ wts, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ inv_perm, int bm, int big,
     Tile* __restrict__ tiles, Ctrl* ctrl, const uint16_t* __restrict__ x, int H,
-    uint8_t* __restrict__ xq) {
+    uint8_t* __restrict__ xq, const uint16_t* __restrict__ wg, float* __restrict__ logits_out) {
   constexpr int NW = 16;
   __shared__ __attribute__((aligned(16))) int s_ids[kRouteSmallMax];
+  __shared__ __attribute__((aligned(16))) float lgs[kFusedRouterMaxTE];
+  __shared__ __attribute__((aligned(16))) float rpart[NW][256];
   __shared__ __attribute__((aligned(16))) float gscr[NW][kGateScratch];
   __shared__ int hist[1024];
   __shared__ int run[1024];  // offsets of the experts
@@ -397,10 +505,18 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   if (blockIdx.x == 0) {  // steps 1-4; in FP8 mode block 1 quantises x
     hist[t] = 0;
 
+    // 0. the router GEMM into LDS
+    if (wg) {
+      router_logits_block(x, wg, T, H, E, lgs, rpart);
+      __syncthreads();
+      if (logits_out)
+        for (int i = t; i < T * E; i += 1024) logits_out[i] = lgs[i];
+    }
     // 1. gating (or the given ids)
-    if (logits) {
+    const float* lsrc = wg ? lgs : logits;
+    if (lsrc) {
       for (int tok = w; tok < T; tok += NW)
-        gate_token(logits + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
+        gate_token(lsrc + (size_t)tok * E, E, k, renorm, ids + (size_t)tok * k,
                    wts + (size_t)tok * k, s_ids + tok * k, gscr[w]);
     } else if (t < n) {
       s_ids[t] = ids[t];
@@ -515,11 +631,14 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                               float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                               int32_t* inv_perm, int bm, bool big, Tile* tiles, Ctrl* ctrl,
-                              const uint16_t* x, int H, uint8_t* xq, hipStream_t st) {
+                              const uint16_t* x, int H, uint8_t* xq, const uint16_t* wg,
+                              float* logits_out, hipStream_t st) {
   if ((long)T * k > kRouteSmallMax || E > 1024) return hipErrorInvalidValue;
+  if (wg && ((long)T * E > kFusedRouterMaxTE || (long)E * H > kFusedRouterMaxEH || !x || H % 128))
+    return hipErrorInvalidValue;
   route_small_kernel<<<xq ? 2 : 1, 1024, 0, st>>>(logits, T, E, k, renorm, ids, w, counts,
                                                  offsets, sorted_ids, inv_perm, bm, big ? 1 : 0,
-                                                 tiles, ctrl, x, H, xq);
+                                                 tiles, ctrl, x, H, xq, wg, logits_out);
   return hipGetLastError();
 }
 

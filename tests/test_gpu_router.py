@@ -22,7 +22,8 @@ import torch
 import moe_layer_gating_amd as moe
 import moe_workloads as wl
 import oracle
-from gpu_helpers import BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, rel_inf, say, upload
+from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, assert_grouping,
+                         rel_inf, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,9 +82,20 @@ def test_router_zero_tokens_is_noop():
 
 LAYERS = [
     # name, T, H, E, k, I, mode, routing
+    # router computed inside the one-block front kernel (bf16 layers, T*k <=
+    # 256, T*E <= 4096, E*H <= 131072): at the limits, ragged expert and
+    # token tiles, K split over fewer ranges than waves, and whole 4-tile
+    # items per wave (E = 1024)
     ("bf16_decode_router", 8, 1024, 8, 2, 512, BF16, "uniform"),
     ("fp8_decode_router", 16, 1024, 64, 8, 256, FP8, "uniform"),
+    ("fp8_front_router_max_te", 32, 1024, 128, 8, 256, FP8, "uniform"),
+    ("bf16_front_router_e1024", 4, 128, 1024, 16, 128, BF16, "uniform"),
+    ("bf16_front_router_ragged", 3, 384, 33, 5, 128, BF16, "uniform"),
+    # separate router kernel: fp32, T*E or E*H just past the front's limits,
+    # many pairs
     ("f32_tiny_router", 16, 128, 8, 2, 256, F32, "uniform"),
+    ("fp8_router_past_te", 33, 256, 128, 4, 128, FP8, "uniform"),
+    ("fp8_router_past_eh", 1, 4096, 64, 8, 256, FP8, "uniform"),
     ("fp8_mixed_router", 512, 768, 128, 8, 256, FP8, "uniform"),
     ("fp8_prefill_router", 600, 512, 256, 8, 256, FP8, "uniform"),
 ]
@@ -99,9 +111,15 @@ def test_fused_forward_router(c):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     say("fused router", name)
+    shape = moe.make_shape(T, H, E, k, I, mode)
+    ws = moe.workspace(shape)
     out = moe.moe_fused_forward_router(D["x"], wg, D["w13"], D["w13_scale"], D["w2"],
-                                       D["w2_scale"], k, logits=lg, topk_ids=ids, topk_weights=w)
+                                       D["w2_scale"], k, logits=lg, topk_ids=ids, topk_weights=w,
+                                       ws=ws)
     torch.cuda.synchronize()
+    views = moe.routing_from_workspace(ws, T, E, k)
+    grp = {n: views[n].cpu().numpy().copy() for n in ("counts", "offsets", "sorted_ids",
+                                                      "inv_perm")}
     g = lg.cpu().numpy()
     exact = oracle.router_logits(mode, L["x"], L["wg"])
     b = _bound(L["x"], L["wg"], mode, H)
@@ -110,6 +128,14 @@ def test_fused_forward_router(c):
     ref = oracle.forward(mode, L["x"], g, L["w13"], L["w13_scale"], L["w2"], L["w2_scale"], k)
     assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
     assert np.max(np.abs(w.cpu().numpy() - ref["topk_weights"])) <= 1e-6
+    assert_grouping(grp, ref["counts"], ref["offsets"], ref["sorted_ids"], ref["inv_perm"])
+    # without the logits output the call computes the same layer
+    ids2 = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out2 = moe.moe_fused_forward_router(D["x"], wg, D["w13"], D["w13_scale"], D["w2"],
+                                        D["w2_scale"], k, topk_ids=ids2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids2, ids)
+    assert torch.equal(out2.view(torch.int16) if mode else out2, out.view(torch.int16) if mode else out)
     og = oracle.to_f64(act_to_numpy(out, mode), mode)
     err = rel_inf(og, ref["out_exact"])
     say("  rel err", err)
