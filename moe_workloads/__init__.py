@@ -195,3 +195,59 @@ def planted_logits(T, E, k, counts, seed=0):
 def scaled(name, T, H, E, k, I, mode, routing="uniform", seed=0):
     """A layer of arbitrary shape drawn with the same recipe."""
     return LayerSpec(name, T, H, E, k, I, mode, routing=routing, seed=seed)
+
+
+# --------------------------------------------------------------------------
+# Inputs of the inverse rotary embedding + per-head FP8 quantisation step.
+# x ~ N(0, 1) drawn in fp32 and rounded to bf16; positions: a prefill batch
+# takes consecutive positions from a seeded start, a decode batch one seeded
+# position per token; the cos/sin table holds, per position p and pair i,
+# cos(p * base^(-2i/rot_dim)) then sin(...), evaluated in float64 and rounded
+# once to fp32 (base 10000, the usual rotary schedule).  The table is an
+# input of the step, like the router logits of the layer.
+@dataclasses.dataclass(frozen=True)
+class RopeSpec:
+    name: str
+    T: int
+    n_heads: int
+    head_dim: int
+    rot_dim: int
+    max_pos: int
+    interleaved: bool = False
+    positions: str = "prefill"  # "prefill" | "random"
+    seed: int = 0
+
+
+ROPE_WORKLOADS = {
+    # a 4096-token prefill batch, 32 heads of 128 values rotated in full
+    "rope_prefill": RopeSpec("rope_prefill", 4096, 32, 128, 128, 8192),
+    # a 16-token decode batch at scattered positions
+    "rope_decode": RopeSpec("rope_decode", 16, 32, 128, 128, 8192, positions="random"),
+}
+
+
+def rope_table(max_pos, rot_dim, base=10000.0):
+    half = rot_dim // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / rot_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.ascontiguousarray(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32))
+
+
+def make_rope(spec: RopeSpec):
+    root = np.random.SeedSequence(spec.seed)
+    ss_x, ss_p = root.spawn(2)
+    x32 = _normal(ss_x, (spec.T, spec.n_heads, spec.head_dim), 1.0)
+    x = to_bf16_bits(x32.reshape(spec.T, -1)).reshape(x32.shape)
+    g = np.random.Generator(np.random.PCG64(ss_p))
+    if spec.positions == "prefill":
+        start = int(g.integers(0, max(1, spec.max_pos - spec.T + 1)))
+        pos = np.arange(start, start + spec.T) % spec.max_pos
+    else:
+        pos = g.integers(0, spec.max_pos, spec.T)
+    return dict(spec=spec, x=np.ascontiguousarray(x), positions=pos.astype(np.int32),
+                cos_sin=rope_table(spec.max_pos, spec.rot_dim))
+
+
+def scaled_rope(name, T, n_heads, head_dim, rot_dim, max_pos, interleaved=False,
+                positions="random", seed=0):
+    return RopeSpec(name, T, n_heads, head_dim, rot_dim, max_pos, interleaved, positions, seed)

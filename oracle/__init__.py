@@ -70,6 +70,7 @@ def _load():
         lib.oracle_w2.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i64, P, P]
         lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         lib.oracle_combine_f32.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        lib.oracle_inv_rope_fp8.argtypes = [P, P, P] + [i32] * 6 + [P, P, P]
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [i32] * 7 + [P] * 16
         _lib = lib
@@ -267,6 +268,28 @@ def forward(mode, x, logits, w13, w13_scale, w2_, w2_scale, k, renormalize=True)
     if rc != 0:
         raise MemoryError("oracle_forward: allocation failed")
     return r
+
+
+def inv_rope_fp8(x, positions, cos_sin, rot_dim=None, interleaved=False):
+    """Inverse rotary embedding then per-(token, head) e4m3 quantisation.
+
+    x [T, n_heads, head_dim] bf16 bits (uint16); positions [T] int32;
+    cos_sin [max_pos, rot_dim] fp32 (cosines, then sines, of the pair
+    angles).  Returns (codes uint8 [T, n_heads, head_dim], scales fp32
+    [T, n_heads], y fp32 [T, n_heads, head_dim] before quantisation)."""
+    x = _c(x, np.uint16)
+    T, nh, hd = x.shape
+    cs = _c(cos_sin, np.float32)
+    max_pos, rd = cs.shape
+    assert rot_dim is None or rot_dim == rd
+    pos = _c(positions, np.int32)
+    assert pos.shape == (T,)
+    codes = np.empty((T, nh, hd), np.uint8)
+    scales = np.empty((T, nh), np.float32)
+    y = np.empty((T, nh, hd), np.float32)
+    _load().oracle_inv_rope_fp8(_p(x), _p(pos), _p(cs), T, nh, hd, rd, max_pos,
+                                int(bool(interleaved)), _p(y), _p(codes), _p(scales))
+    return codes, scales, y
 
 
 def to_f64(a, mode):

@@ -498,6 +498,78 @@ int oracle_forward(int wdtype, int T, int H, int E, int k, int I, int renormaliz
 }
 
 /* ------------------------------------------------------------------------ */
+/* The second fused kernel of the pages: inverse rotary position embedding   */
+/* followed by per-head FP8 quantisation, over a token count that changes    */
+/* from call to call (codebridge-ai.com, "aws-moe-kernel-wgmma-triton-ttft", */
+/* section "3. Kill JIT recompilation": a fused rotary-embedding plus FP8    */
+/* quantisation kernel; agentic-affairs.com, "Removing recompilation         */
+/* improves the first-token result": the kernel's variable-length            */
+/* parameters; modelsatwork.news, "The three changes").  The pages give no   */
+/* formula; Readings:                                                         */
+/*  - x [T, n_heads, head_dim] bf16, one position per token (int32);          */
+/*  - the rotary embedding rotates coordinate pairs of the first rot_dim     */
+/*    values of each head by the angle of the token's position; the angle's  */
+/*    cosine and sine come from a table cos_sin [max_pos, rot_dim] fp32,     */
+/*    row p = cos of the rot_dim/2 pair angles, then their sines;             */
+/*  - pairs are (i, i + rot_dim/2) ("rotate half"), or (2i, 2i+1) when       */
+/*    interleaved = 1; values past rot_dim pass through;                      */
+/*  - "inverse" is the rotation by the negative angle (the transpose of the  */
+/*    forward rotation), which undoes a forward rotary embedding:            */
+/*      y_a = x_a c + x_b s,   y_b = x_b c - x_a s   for pair (a, b);        */
+/*    each product and the sum are single fp32 operations (no fused          */
+/*    multiply-add), since the codes are decided on y;                        */
+/*  - "per head" quantisation: one dynamic scale per (token, head), the      */
+/*    same rule as the layer's activations: A = max |y| over the head,       */
+/*    s = fl32(A / 448), codes e4m3(fl32(y * fl32(448 / A))), A = 0 giving    */
+/*    s = 1 and multiplier 1.                                                 */
+/* A position outside [0, max_pos) breaks the contract; it is clamped into   */
+/* the table.  Writes codes [T, n_heads, head_dim], scales [T, n_heads] and,  */
+/* if y_out is non-NULL, the rotated values y (fp32) before quantisation.    */
+/* ------------------------------------------------------------------------ */
+void oracle_inv_rope_fp8(const uint16_t* x, const int32_t* positions, const float* cos_sin,
+                         int T, int n_heads, int head_dim, int rot_dim, int max_pos,
+                         int interleaved, float* y_out, uint8_t* codes, float* scales) {
+  const int half = rot_dim / 2;
+  float* y = (float*)malloc(sizeof(float) * (size_t)(head_dim > 0 ? head_dim : 1));
+  for (long th = 0; th < (long)T * n_heads; th++) {
+    const long t = th / n_heads;
+    long p = positions[t];
+    if (p < 0) p = 0;
+    if (p >= max_pos) p = max_pos - 1;
+    const float* cs = cos_sin + (size_t)p * rot_dim;
+    const uint16_t* xh = x + (size_t)th * head_dim;
+    for (int d = 0; d < head_dim; d++) y[d] = (float)oracle_bf16_decode(xh[d]);
+    for (int i = 0; i < half; i++) {
+      const int a = interleaved ? 2 * i : i;
+      const int b = interleaved ? 2 * i + 1 : i + half;
+      const float xa = (float)oracle_bf16_decode(xh[a]);
+      const float xb = (float)oracle_bf16_decode(xh[b]);
+      volatile float c = cs[i], s = cs[half + i];
+      volatile float p1 = xa * c, p2 = xb * s, p3 = xb * c, p4 = xa * s;
+      volatile float ya = p1 + p2, yb = p3 - p4;
+      y[a] = ya;
+      y[b] = yb;
+    }
+    double A = 0.0;
+    for (int d = 0; d < head_dim; d++)
+      if (fabs((double)y[d]) > A) A = fabs((double)y[d]);
+    float Af = (float)A; /* exact: A is an fp32 value */
+    volatile float sc = 1.0f, r = 1.0f;
+    if (Af > 0.0f) {
+      sc = Af / 448.0f;
+      r = 448.0f / Af;
+    }
+    for (int d = 0; d < head_dim; d++) {
+      volatile float q = y[d] * r;
+      codes[(size_t)th * head_dim + d] = oracle_e4m3_encode(q);
+      if (y_out) y_out[(size_t)th * head_dim + d] = y[d];
+    }
+    scales[th] = sc;
+  }
+  free(y);
+}
+
+/* ------------------------------------------------------------------------ */
 /* array forms of the codecs (for exhaustive checks)                         */
 /* ------------------------------------------------------------------------ */
 void oracle_e4m3_encode_array(const float* v, long n, uint8_t* out) {
