@@ -223,6 +223,36 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
  * MOE_OK with nothing enqueued. */
 int moe_act_quant_e4m3(const void* a, int64_t n, uint8_t* codes, float* scales, void* stream);
 
+/* Inverse rotary position embedding fused with per-head FP8 quantisation:
+ * the pages' second fused kernel, whose token count changes from call to
+ * call (codebridge-ai.com, "aws-moe-kernel-wgmma-triton-ttft", section "3.
+ * Kill JIT recompilation"; agentic-affairs.com, "Removing recompilation
+ * improves the first-token result").  Compiled ahead of time; T and the
+ * positions are run-time arguments, so no token count is a specialisation.
+ *   x         [T, n_heads, head_dim] bf16 in, contiguous
+ *   positions [T] int32: token t uses row positions[t] of the table (a value
+ *             outside [0, max_pos) breaks the contract and is clamped)
+ *   cos_sin   [max_pos, rot_dim] fp32: per position, the cosines of the
+ *             rot_dim/2 pair angles, then their sines
+ *   codes     [T, n_heads, head_dim] OCP e4m3fn codes out
+ *   scales    [T, n_heads] fp32 out
+ * Over the first rot_dim values of each head, a pair (a, b) -- (i, i +
+ * rot_dim/2), or (2i, 2i+1) with interleaved = 1 -- becomes y_a = x_a c +
+ * x_b s, y_b = x_b c - x_a s (the rotation by the negative angle: the
+ * inverse of a forward rotary embedding), each product and sum a single
+ * fp32 operation; values past rot_dim pass through.  Each (token, head) is
+ * then quantised with its own scale: A = max |y| over the head, scales =
+ * fl32(A/448), codes = e4m3(fl32(y * fl32(448/A))) rounded to nearest even
+ * and saturated (A = 0: scale 1).
+ * Limits: head_dim and rot_dim multiples of 16, 16 <= rot_dim <= head_dim <=
+ * 512 (MOE_ERR_UNSUPPORTED otherwise); T >= 0, n_heads >= 1, max_pos >= 1,
+ * T * n_heads < 2^31, pointers 16-byte aligned (MOE_ERR_INVALID_ARG).
+ * T = 0 returns MOE_OK with nothing enqueued. */
+int moe_inv_rope_fp8_quant(const void* x, const int32_t* positions, const float* cos_sin,
+                           int32_t T, int32_t n_heads, int32_t head_dim, int32_t rot_dim,
+                           int32_t max_pos, int32_t interleaved, uint8_t* codes, float* scales,
+                           void* stream);
+
 /* The whole layer in one call, the single batched operation that merges
  * routing, data shuffling and the expert calculations (readmex.ai, "AWS
  * details fused MoE kernel optimizations on SageMaker, up to 10% throughput

@@ -44,7 +44,7 @@ EXPORTS = ("moe_check_shape", "moe_workspace_bytes", "moe_status_string",
            "moe_align_sort", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_w2", "moe_combine",
            "moe_act_quant_e4m3",
            "moe_fused_forward", "moe_fused_forward_events", "moe_router_logits",
-           "moe_fused_forward_router", "moe_fused_forward_noalloc")
+           "moe_fused_forward_router", "moe_fused_forward_noalloc", "moe_inv_rope_fp8_quant")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 # host-only calls whose return type is not a moe_status
 _NON_STATUS = ("moe_workspace_bytes", "moe_status_string", "moe_align_sort_workspace_bytes")
@@ -78,6 +78,7 @@ def lib():
         L.moe_act_quant_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
         L.moe_fused_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_fused_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        L.moe_inv_rope_fp8_quant.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
         L.moe_router_logits.argtypes = [S, P, P, P, P, sz, P]
         L.moe_fused_forward_router.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_fused_forward_events.argtypes = [S, P, P, P, P, P, P, P, P, P, P, sz, P,
@@ -291,6 +292,23 @@ def moe_fused_forward_noalloc(x, logits, w13, w13_scale, w2, w2_scale, k, out,
                                            _ptr(topk_ids), _ptr(topk_weights), _stream()),
            "moe_fused_forward_noalloc")
     return out
+
+
+def moe_inv_rope_fp8_quant(x, positions, cos_sin, interleaved=False, codes=None, scales=None):
+    """Inverse rotary embedding + per-(token, head) e4m3 quantisation.
+    x [T, n_heads, head_dim] bf16, positions [T] int32, cos_sin [max_pos,
+    rot_dim] fp32 -> (codes uint8 [T, n_heads, head_dim], scales fp32
+    [T, n_heads])."""
+    T, nh, hd = x.shape
+    max_pos, rot = cos_sin.shape
+    if codes is None:
+        codes = torch.empty((T, nh, hd), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T, nh), dtype=torch.float32, device=x.device)
+    _check(lib().moe_inv_rope_fp8_quant(_ptr(x), _ptr(positions), _ptr(cos_sin), T, nh, hd, rot,
+                                        max_pos, int(bool(interleaved)), _ptr(codes),
+                                        _ptr(scales), _stream()), "moe_inv_rope_fp8_quant")
+    return codes, scales
 
 
 def moe_router_logits(x, wg, E=None, k=1, ws=None, logits=None):

@@ -374,6 +374,26 @@ int moe_act_quant_e4m3(const void* a, int64_t n, uint8_t* codes, float* scales, 
   return MOE_OK;
 }
 
+int moe_inv_rope_fp8_quant(const void* x, const int32_t* positions, const float* cos_sin,
+                           int32_t T, int32_t n_heads, int32_t head_dim, int32_t rot_dim,
+                           int32_t max_pos, int32_t interleaved, uint8_t* codes, float* scales,
+                           void* stream) {
+  if (T < 0 || n_heads < 1 || max_pos < 1 || (interleaved != 0 && interleaved != 1))
+    return MOE_ERR_INVALID_ARG;
+  if ((long)T * n_heads >= (1L << 31)) return MOE_ERR_INVALID_ARG;
+  if (head_dim % 16 || head_dim < 16 || head_dim > 512 || rot_dim % 16 || rot_dim < 16 ||
+      rot_dim > head_dim)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !positions || !cos_sin || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(positions) || !aligned16(cos_sin) || !aligned16(codes) ||
+      !aligned16(scales))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_inv_rope_fp8(reinterpret_cast<const uint16_t*>(x), positions, cos_sin,
+                                        T, n_heads, head_dim, rot_dim, max_pos, interleaved != 0,
+                                        codes, scales, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int moe_combine(const moe_shape* s, const float* y, const int32_t* inv_perm,
                 const float* topk_weights, void* out, void* stream) {
   int rc = moe_check_shape(s);

@@ -196,6 +196,11 @@ hipError_t launch_w2_tiles(int mode, int bm, const void* b, const void* w2, cons
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H,
                            int I, const uint32_t* act_amax_bits, void* y, bool y_bf16,
                            hipEvent_t e0, hipEvent_t e1, hipStream_t st);
+// Inverse rotary embedding + per-head e4m3 quantisation (rope.hip); shapes
+// already checked by the caller (head_dim / 8 <= 64 lanes per head).
+hipError_t launch_inv_rope_fp8(const uint16_t* x, const int32_t* positions, const float* cos_sin,
+                               int T, int n_heads, int head_dim, int rot_dim, int max_pos,
+                               bool interleaved, uint8_t* codes, float* scales, hipStream_t st);
 // y [T*k,H] in sorted order, fp32 or (y_bf16, not in fp32 mode) bf16.
 hipError_t launch_combine(int mode, const void* y, bool y_bf16, const int32_t* inv_perm,
                           const float* w, int T, int H, int k, void* out, hipStream_t st);

@@ -168,6 +168,23 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(L):
                                        None, None, None, None) == -2
 
 
+def test_inv_rope_rejects_before_launch(L):
+    good = _fake(0x100000)
+    odd = _fake(0x100004)
+    f = L.moe_inv_rope_fp8_quant
+    assert f(good, good, good, 4, 8, 100, 64, 16, 0, good, good, None) == -2  # head_dim % 16
+    assert f(good, good, good, 4, 8, 128, 136, 16, 0, good, good, None) == -2  # rot > head
+    assert f(good, good, good, 4, 8, 1024, 128, 16, 0, good, good, None) == -2  # head > 512
+    assert f(good, good, good, 4, 8, 128, 0, 16, 0, good, good, None) == -2
+    assert f(good, good, good, 4, 0, 128, 128, 16, 0, good, good, None) == -1
+    assert f(good, good, good, 4, 8, 128, 128, 0, 0, good, good, None) == -1
+    assert f(good, good, good, 4, 8, 128, 128, 16, 2, good, good, None) == -1
+    assert f(None, good, good, 4, 8, 128, 128, 16, 0, good, good, None) == -1
+    assert f(good, good, good, 4, 8, 128, 128, 16, 0, odd, good, None) == -1
+    assert f(good, good, good, -1, 8, 128, 128, 16, 0, good, good, None) == -1
+    assert f(None, None, None, 0, 8, 128, 128, 16, 0, None, None, None) == 0  # T = 0
+
+
 def test_act_quant_rejects_before_launch(L):
     good = _fake(0x100000)
     odd = _fake(0x100004)
