@@ -48,7 +48,10 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   the front kernel computes the logits itself, one launch
                   fewer), per step, and the router GEMM alone, as separate
                   figures (also in each sub-record);
-  sub_records  -- the same step figures for the sub-record layers.
+  sub_records  -- the same step figures for the sub-record layers; for
+                  rope_prefill / rope_decode, the inverse rotary embedding +
+                  per-head FP8 quantisation step (moe_inv_rope_fp8_quant):
+                  its launch time and bytes against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -401,14 +404,73 @@ def measure(name, args, H_, full):
     return rec
 
 
+def measure_rope(name, args, H_):
+    """Time K launches of the inverse rotary embedding + per-head FP8
+    quantisation step (moe_inv_rope_fp8_quant) on a seeded batch; the
+    kernel's duration comes from an event pair around the K launches on the
+    launch stream.  Algorithmic bytes: x read once (2 B per value), codes
+    written (1 B per value), one fp32 scale per (token, head), the positions,
+    and the table rows of the batch's distinct positions."""
+    import numpy as np
+    import torch
+
+    import moe_layer_gating_amd as moe
+    import moe_workloads as wl
+
+    spec = wl.ROPE_WORKLOADS[name]
+    log("generating", name)
+    R = wl.make_rope(spec)
+    x = torch.from_numpy(R["x"].view(np.int16)).view(torch.bfloat16).cuda()
+    pos = torch.from_numpy(R["positions"]).cuda()
+    cs = torch.from_numpy(R["cos_sin"]).cuda()
+    T, nh, hd, rot = spec.T, spec.n_heads, spec.head_dim, spec.rot_dim
+    codes = torch.empty((T, nh, hd), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((T, nh), dtype=torch.float32, device="cuda")
+
+    def launch():
+        moe.moe_inv_rope_fp8_quant(x, pos, cs, interleaved=spec.interleaved, codes=codes,
+                                   scales=scales)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    e = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for ev in e:
+        assert H_.hipEventCreate(ctypes.byref(ev)) == 0
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    reps = max(args.steps, 50)
+    t0 = time.perf_counter()
+    H_.hipEventRecord(e[0], stream)
+    for _ in range(reps):
+        launch()
+    H_.hipEventRecord(e[1], stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    f = ctypes.c_float()
+    assert H_.hipEventElapsedTime(ctypes.byref(f), e[0], e[1]) == 0
+    for ev in e:
+        H_.hipEventDestroy(ev)
+    ms = f.value / reps
+    n_pos = int(np.unique(R["positions"]).size)
+    nbytes = T * nh * hd * 3 + T * nh * 4 + T * 4 + n_pos * rot * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "%s: T=%d heads=%d head_dim=%d rot_dim=%d max_pos=%d" % (
+                name, T, nh, hd, rot, spec.max_pos),
+            "dtype": "bf16 in, fp8e4m3 out", "ms_per_launch": ms, "wall_ms_per_launch": wall,
+            "tokens_per_s": T / (ms * 1e-3), "alg_bytes": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "inv_rope_fp8_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_fp8")
-    ap.add_argument("--sub", default="decode_bf16",
-                    help="comma-separated layers measured as sub-records, or 'none'")
+    ap.add_argument("--sub", default="decode_bf16,rope_prefill",
+                    help="comma-separated layers (or rope_prefill / rope_decode, the inverse "
+                         "rotary embedding + FP8 step) measured as sub-records, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
@@ -448,6 +510,9 @@ def main():
 
     subs = {}
     for name in [n for n in args.sub.split(",") if n and n != "none" and n != args.workload]:
+        if name.startswith("rope_"):
+            subs[name] = measure_rope(name, args, H_)
+            continue
         r = measure(name, args, H_, full=False)
         del r["_layer"]
         gc.collect()

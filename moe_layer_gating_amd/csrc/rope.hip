@@ -22,17 +22,19 @@
 // dynamic scale: A = max |y| over the head, scale = fl32(A / 448), codes
 // e4m3(fl32(y * fl32(448 / A))), A = 0 giving scale 1.
 //
-// Work decomposition: one thread per 16-byte chunk (8 values) of a head; a
-// head occupies G = next power of two >= head_dim / 8 consecutive lanes, so
-// its amax is a butterfly over G lanes.  For the rotate-half pairing a chunk
-// in the first half of the rotated range pairs with the chunk rot_dim/16
-// further on, and each thread loads its partner chunk itself (the same cache
-// lines as its neighbours' chunks).  Memory traffic is one read of x, one
-// write of the codes and scales, and the table rows of the batch's positions.
+// Memory traffic is one read of x, one write of the codes and scales, and
+// the table rows of the batch's positions.
 #include "moe_common.h"
 
 namespace moe {
 
+// Rotate-half pairing: a head's work units are its rot_dim/16 chunk pairs
+// (chunk u with chunk u + rot_dim/16: the pairs (8u + j, 8u + j +
+// rot_dim/2), j < 8) and its (head_dim - rot_dim)/8 pass-through chunks; one
+// thread per unit, so each value and each table entry is loaded once.
+// Interleaved pairing: one thread per chunk (its pairs lie inside it).  A
+// head's units occupy G = next power of two lanes, so its amax is a
+// butterfly over G lanes.
 template <bool INTER>
 __global__ __launch_bounds__(256) void inv_rope_fp8_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ positions,
@@ -44,29 +46,37 @@ __global__ __launch_bounds__(256) void inv_rope_fp8_kernel(
   // which keep the default), so the arithmetic below uses plain operators.
 #pragma clang fp contract(off)
   const int lane = lane_id();
-  const int q = lane & (G - 1);  // chunk of the head
+  const int u = lane & (G - 1);  // work unit of the head
   const long th = ((long)blockIdx.x * blockDim.x + threadIdx.x) / G;
-  const int chunks = head_dim / 8;
-  const bool live = th < n_heads_total && q < chunks;
-  float y[8];
+  const int half = rot_dim / 2;
+  const int h8 = rot_dim / 16;  // chunk pairs (rotate half)
+  const int units = INTER ? head_dim / 8 : h8 + (head_dim - rot_dim) / 8;
+  const bool live = th < n_heads_total && u < units;
+  // chunk c0 holds y[0..8); rotate-half pair units also chunk c1 = c0 + h8
+  // with y[8..16)
+  const int c0 = INTER || u < h8 ? u : u + h8;
+  const bool pair = !INTER && u < h8;
+  float y[16];
   float m = 0.f;
   if (live) {
     const long t = th / n_heads;
     int p = positions[t];
     p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
     const float* cs = cos_sin + (size_t)p * rot_dim;
-    const int half = rot_dim / 2;
     const uint16_t* xh = x + (size_t)th * head_dim;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(xh + 8 * q);
+    const i32x4 v0 = *reinterpret_cast<const i32x4*>(xh + 8 * c0);
+    const i32x4 v1 = pair ? *reinterpret_cast<const i32x4*>(xh + 8 * (c0 + h8)) : v0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      y[2 * j] = bf16_to_f32((uint16_t)((uint32_t)v[j] & 0xffffu));
-      y[2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v[j] >> 16));
+      y[2 * j] = bf16_to_f32((uint16_t)((uint32_t)v0[j] & 0xffffu));
+      y[2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v0[j] >> 16));
+      y[8 + 2 * j] = bf16_to_f32((uint16_t)((uint32_t)v1[j] & 0xffffu));
+      y[8 + 2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v1[j] >> 16));
     }
     if (INTER) {
-      if (8 * q < rot_dim) {  // pairs (2i, 2i+1), i = 4q + j
-        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * q);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + half + 4 * q);
+      if (8 * c0 < rot_dim) {  // pairs (2i, 2i+1), i = 4 c0 + j
+        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * c0);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + half + 4 * c0);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const float xa = y[2 * j], xb = y[2 * j + 1];
@@ -74,51 +84,51 @@ __global__ __launch_bounds__(256) void inv_rope_fp8_kernel(
           y[2 * j + 1] = xb * c[j] - xa * s[j];
         }
       }
-    } else if (8 * q < rot_dim) {  // pairs (i, i + half); half is a multiple of 8
-      const bool first = 8 * q < half;
-      const int pq = first ? q + half / 8 : q - half / 8;  // partner chunk
-      const int i0 = first ? 8 * q : 8 * q - half;         // pair index of value 0
-      const i32x4 pv = *reinterpret_cast<const i32x4*>(xh + 8 * pq);
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + i0);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + i0 + 4);
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + half + i0);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + half + i0 + 4);
+    } else if (pair) {  // pairs (8 c0 + j, 8 c0 + j + half)
+      const f32x4 ca = *reinterpret_cast<const f32x4*>(cs + 8 * c0);
+      const f32x4 cb = *reinterpret_cast<const f32x4*>(cs + 8 * c0 + 4);
+      const f32x4 sa = *reinterpret_cast<const f32x4*>(cs + half + 8 * c0);
+      const f32x4 sb = *reinterpret_cast<const f32x4*>(cs + half + 8 * c0 + 4);
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const uint32_t u = (uint32_t)pv[j / 2];
-        const float other = bf16_to_f32((uint16_t)(j & 1 ? u >> 16 : u & 0xffffu));
-        const float c = j < 4 ? c0[j] : c1[j - 4], s = j < 4 ? s0[j] : s1[j - 4];
-        // first half: this value is x_a, the partner x_b; second half: this
-        // value is x_b, the partner x_a
-        y[j] = first ? y[j] * c + other * s : y[j] * c - other * s;
+        const float c = j < 4 ? ca[j] : cb[j - 4], s = j < 4 ? sa[j] : sb[j - 4];
+        const float xa = y[j], xb = y[8 + j];
+        y[j] = xa * c + xb * s;
+        y[8 + j] = xb * c - xa * s;
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; j++) m = fmaxf(m, fabsf(y[j]));
+    for (int j = 0; j < 16; j++)
+      if (j < 8 || pair) m = fmaxf(m, fabsf(y[j]));
   }
   // amax over the head's G lanes (G divides 64; groups are lane-aligned)
   for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (!live) return;
   const float sc = m > 0.f ? m / 448.0f : 1.0f;
   const float r = m > 0.f ? 448.0f / m : 1.0f;
-  float f[8];
+  uint8_t* ch = codes + (size_t)th * head_dim;
 #pragma unroll
-  for (int j = 0; j < 8; j++) f[j] = __builtin_amdgcn_fmed3f(y[j] * r, -448.0f, 448.0f);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-  *reinterpret_cast<uint2*>(codes + (size_t)th * head_dim + 8 * q) =
-      make_uint2((uint32_t)lo, (uint32_t)hi);
-  if (q == 0) scales[th] = sc;
+  for (int k8 = 0; k8 < 2; k8++) {
+    if (k8 == 1 && !pair) break;
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      f[j] = __builtin_amdgcn_fmed3f(y[8 * k8 + j] * r, -448.0f, 448.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    *reinterpret_cast<uint2*>(ch + 8 * (c0 + k8 * h8)) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+  if (u == 0) scales[th] = sc;
 }
 
 hipError_t launch_inv_rope_fp8(const uint16_t* x, const int32_t* positions, const float* cos_sin,
                                int T, int n_heads, int head_dim, int rot_dim, int max_pos,
                                bool interleaved, uint8_t* codes, float* scales, hipStream_t st) {
-  const int chunks = head_dim / 8;
+  const int units = interleaved ? head_dim / 8 : rot_dim / 16 + (head_dim - rot_dim) / 8;
   int G = 1;
-  while (G < chunks) G <<= 1;
+  while (G < units) G <<= 1;
   if (G > kWave) return hipErrorInvalidValue;
   const long heads = (long)T * n_heads;
   const long threads = heads * G;
