@@ -33,14 +33,16 @@
 // FP8 gate/up projection (kFp8ViaBf16): the token stage is widened to bf16
 // as it is written to LDS and the weight fragments are widened in registers;
 // the products then go through the bf16 MFMA, whose sums are exact where the
-// FP8 MFMA's are not.  A widened row is 256 bytes (16 chunks, chunk q holding
-// K values 8q .. 8q+7) and keeps chunk q at slot rot(q) ^ vswz(r), with
-// rot(q) = (q >> 1) | ((q & 1) << 3) and, for m = r & 15, vswz(r) = swz(m) |
-// (((m ^ (m >> 1)) & 1) << 3).  The 8 lanes staging one row store chunks 2c
-// (then 2c+1), which rot spreads over all 8 slots of a 128-byte bank row (a
-// plain XOR layout leaves them on 4: two-way store conflicts); the fragment
-// reads of 8, 16 and 32 consecutive lanes, and the stores, hit distinct
-// 16-byte bank groups.
+// FP8 MFMA's are not.  A widened row has 16 chunks of 16 bytes (chunk q
+// holding K values 8q .. 8q+7), kept as two planes with the geometry of an
+// FP8 stage: plane q & 1 (the odd chunks BM * 128 bytes after the even
+// ones), 128-byte rows, chunk q at slot (q >> 1) ^ swz(r).  A thread staging
+// FP8 chunk c of a row stores its bf16 chunks 2c and 2c+1 at slot c ^ swz(r)
+// of the two planes, and MFMA u of lane group g reads chunk 4g + u: plane
+// u & 1, slot (2g + u/2) ^ swz(r) -- the FP8 stage's store and fragment
+// patterns, whose 16-byte LDS accesses were measured free of bank conflicts
+// on gfx950 (a single 256-byte-row layout measured 2-way conflicts on both
+// its stores and its fragment reads).
 //
 // Launch order: block b takes tile b / NB and weight-row block b % NB, with
 // NB = (rows of the weight matrix) / (128*WN).  Blocks are dealt to the 8 XCDs
@@ -56,12 +58,6 @@ constexpr int kStageB = 128;  // bytes of K per row per stage
 constexpr int kPD = 3;        // weight stages in flight per wave
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-// a function of r & 15, so a fragment read may pass its row within the tile
-__device__ __forceinline__ int vswz(int r) {
-  r &= 15;
-  return ((r ^ (r >> 3)) & 7) | (((r ^ (r >> 1)) & 1) << 3);
-}
-__device__ __forceinline__ int vrot(int q) { return (q >> 1) | ((q & 1) << 3); }
 
 // One 128-byte K stage of a 16x16 output tile: each lane supplies 32 bytes
 // of its row of each operand, as two 16-byte chunks (h = 0, 1).
@@ -113,7 +109,8 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   static_assert(BM / 16 <= MTA && (BM % (32 * WN) == 0 || BM == 16 * WN), "tile shape");
   constexpr bool VIA = MODE == kFp8ViaBf16;
   typedef TileMma<VIA ? MOE_FP8_E4M3 : MODE> M;
-  constexpr int ROWB = VIA ? 2 * kStageB : kStageB;  // LDS bytes per token row
+  constexpr int ROWB = kStageB;        // LDS bytes per token row (per plane when widened)
+  constexpr int PLANE = BM * kStageB;  // widened: the odd bf16 chunks' plane follows
   constexpr int B_BYTES = stage_lds_bytes<MODE, BM>();
   // token rows staged per thread; a stage of fewer than 32*WN rows is staged
   // by the threads with r0 < BM only (whole waves)
@@ -130,13 +127,8 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
 #pragma unroll
   for (int i = 0; i < NB; i++) {
     const int r = r0 + 32 * WN * i;
-    if (VIA) {  // bf16 chunks 2c and 2c+1 of the widened row
-      b_slot[i] = r * ROWB + ((vrot(2 * c) ^ vswz(r)) << 4);
-      b_slot2[i] = r * ROWB + ((vrot(2 * c + 1) ^ vswz(r)) << 4);
-    } else {
-      b_slot[i] = r * ROWB + ((c ^ swz(r)) << 4);
-      b_slot2[i] = 0;
-    }
+    b_slot[i] = r * ROWB + ((c ^ swz(r)) << 4);
+    b_slot2[i] = VIA ? PLANE + b_slot[i] : 0;  // widened: bf16 chunks 2c and 2c+1
   }
   auto stage_b = [&](char* buf, const i32x4* src) {
     if (!ALL_STAGE && r0 >= BM) return;
@@ -216,11 +208,13 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
         for (int u = 0; u < 4; u++) {
           const bf16x8 a0u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a0[2 * u], a0[2 * u + 1]));
           const bf16x8 a1u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a1[2 * u], a1[2 * u + 1]));
-          const int off = b_base + ((vrot(4 * g + u) ^ vswz(r16)) << 4);
+          const char* plane = cur + (u & 1) * PLANE + b_base;
 #pragma unroll
           for (int j = 0; j < MT; j++) {
+            const int sw = (r16 ^ (2 * j + r16h)) & 7;
             const bf16x8 fb = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const i32x4*>(cur + j * 16 * ROWB + off));
+                bf16x8, *reinterpret_cast<const i32x4*>(plane + j * 16 * ROWB +
+                                                        (((2 * g + (u >> 1)) ^ sw) << 4)));
             acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0u, fb, acc[0][j], 0, 0, 0);
             acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1u, fb, acc[1][j], 0, 0, 0);
           }
