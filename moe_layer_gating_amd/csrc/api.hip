@@ -516,11 +516,19 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
   Tile* tl = big ? tiles_big : tiles;
   MOE_TRY(mark(0));
   if (grouping == Grouping::kOneBlock) {
+    // the front kernel's second block quantises a small x; a large one goes
+    // to the grid-wide passes after it (the kernel leaves amax(x) at 0)
+    const bool front_quant = fp8 && (long)T * H <= kFrontQuantMax;
     MOE_TRY(launch_route_small(wg ? nullptr : logits, T, E, k, s->renormalize, ids, wts, counts,
                                offsets, sorted, inv, bm, big, tl, ctrl,
-                               reinterpret_cast<const uint16_t*>(x), H, xq,
+                               reinterpret_cast<const uint16_t*>(x), H,
+                               front_quant ? xq : nullptr,
                                reinterpret_cast<const uint16_t*>(wg), logits_out, st));
     for (int i = 1; i <= 3; i++) MOE_TRY(mark(i));
+    if (fp8 && !front_quant &&
+        (rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,
+                            xq, st)))
+      return rc;
   } else {
     // zeroes the control block
     MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,

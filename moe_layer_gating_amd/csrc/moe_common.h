@@ -13,6 +13,10 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kSkinnyBM = 16;  // sorted positions per tile of the few-token GEMMs
 constexpr int kRouteSmallMax = 256;  // pairs routed by the one-block front kernel
+// x values the one-block front kernel quantises in its second block; a larger
+// x goes to the grid-wide amax and quantisation passes (one block streams
+// about 0.1 TB/s, the grid-wide passes the whole chip's bandwidth)
+constexpr long kFrontQuantMax = 131072;
 constexpr int kSortChunk = 1024;     // pairs per chunk of the many-pair grouping (one per thread)
 constexpr int kChunkSortMin = 8192;  // pairs from which the chunked grouping is used
 constexpr int kTilesBMMin = 64;  // smallest tile of the many-token GEMMs (64 or 128 positions)

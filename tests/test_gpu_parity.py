@@ -68,6 +68,9 @@ CASES = [
     # tiled GEMMs, with the chunked grouping over all 1024 experts
     ("bf16_max_E_k", 16, 128, 1024, 16, 128, BF16, "uniform"),
     ("fp8_max_E_k_multi", 17, 128, 1024, 16, 128, FP8, "uniform"),
+    # one-block front with an x too large for its quantising block (T*H >
+    # 131072): x goes to the grid-wide amax and quantisation passes
+    ("fp8_front_big_x", 64, 4096, 64, 4, 128, FP8, "uniform"),
     ("fp8_tiles_max_E", 1024, 128, 1024, 16, 128, FP8, "uniform"),
 ]
 IDS = [c[0] for c in CASES]
