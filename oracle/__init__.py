@@ -30,26 +30,38 @@ F32, BF16, FP8 = 0, 1, 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, used
+# when MOE_ORACLE_SANITIZE=1 (the process must preload the ASan runtime)
+_LIB_SAN = os.path.join(_HERE, "libmoe_oracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer", "-g"]
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the C oracle into ``oracle/libmoe_oracle.so``."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def _sanitized():
+    return os.environ.get("MOE_ORACLE_SANITIZE") == "1"
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the C oracle into ``oracle/libmoe_oracle.so`` (or, with
+    ``sanitize``, the ASan/UBSan build ``oracle/libmoe_oracle_san.so``)."""
+    lib = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-               "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+               "-shared", "-Wall"] + (_SAN_FLAGS if sanitize else []) + ["-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = _LIB_SAN if _sanitized() else _LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(sanitize=_sanitized())
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_long
         lib.oracle_bf16_round.restype = ctypes.c_uint16
