@@ -101,6 +101,9 @@ def kernel_sources(big):
     return [os.path.join(CSRC, n) for n in names]
 
 
+ROPE_SOURCES = [os.path.join(CSRC, n) for n in ("rope.hip", "moe_common.h")]
+
+
 def sources_sha256(files):
     h = hashlib.sha256()
     for f in files:
@@ -109,7 +112,7 @@ def sources_sha256(files):
     return h.hexdigest()
 
 
-def traffic_for(workload, kernel, big):
+def traffic_for(workload, kernel, files):
     """HBM bytes per launch of the dominant kernel from the stored counter
     runs, or None if there are none or the kernel sources changed since."""
     try:
@@ -119,7 +122,7 @@ def traffic_for(workload, kernel, big):
         return None
     if not rec or rec.get("kernel") != kernel:
         return None
-    if rec.get("sources_sha256") != sources_sha256(kernel_sources(big)):
+    if rec.get("sources_sha256") != sources_sha256(files):
         return None
     return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024
 
@@ -295,7 +298,7 @@ def measure(name, args, H_, full):
                 "peak": peak if mfma_bound else HBM_PEAK_GBS,
                 "unit": "TFLOP/s" if mfma_bound else "GB/s",
                 "frac": w13_tflops / peak if mfma_bound else w13_gbs / HBM_PEAK_GBS,
-                "traffic": traffic_for(spec.name, lay.kernel, lay.big),
+                "traffic": traffic_for(spec.name, lay.kernel, kernel_sources(lay.big)),
                 "bytes_per_launch": w13_bytes, "flops_per_launch": w13_flops, "avg_ms": w13_ms,
                 "hbm_gbs": w13_gbs, "mfma_tflops": w13_tflops, "mfma_peak_tflops": peak,
                 "mfma_issued": "bf16 (e4m3 codes widened)" if mode == 2 else DTYPE_NAME[mode],
@@ -459,7 +462,8 @@ def measure_rope(name, args, H_):
             "dtype": "bf16 in, fp8e4m3 out", "ms_per_launch": ms, "wall_ms_per_launch": wall,
             "tokens_per_s": T / (ms * 1e-3), "alg_bytes": nbytes,
             "roofline": {"bound": "hbm", "kernel": "inv_rope_fp8_kernel", "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}}
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic_for(name, "inv_rope_fp8_kernel", ROPE_SOURCES)}}
 
 
 def main():
