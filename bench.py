@@ -21,8 +21,8 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   per step against 8 TB/s and against the dense MFMA peak of
                   the layer's arithmetic type (FP8 layers: 5.0 PFLOP/s for
                   every flop); layer_mfma_frac_issued prices each GEMM at the
-                  peak of the MFMA type its kernel issues (FP8 gate/up on the
-                  bf16 MFMA, 2.5 PFLOP/s), a secondary figure;
+                  peak of the MFMA type its kernel issues (the few-token FP8
+                  gate/up on the bf16 MFMA, 2.5 PFLOP/s), a secondary figure;
   roofline     -- the dominant kernel (the gate/up GEMM): its algorithmic
                   bytes (or flops) per launch / its average duration, timed
                   with HIP events taken by that kernel's own dispatch in
@@ -70,10 +70,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # dense MFMA peak of the layer's arithmetic type (fp32, bf16, FP8 e4m3)
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 5000.0}
-# peaks of the MFMA types the kernels issue, (gate/up, down): in FP8 mode the
-# gate/up products run on the bf16 MFMA (e4m3 codes widened to bf16, so that
-# the sums behind h are exact); the down projection uses the FP8 MFMA
-ISSUED_PEAK_TFLOPS = {0: (157.3, 157.3), 1: (2500.0, 2500.0), 2: (2500.0, 5000.0)}
+
+
+def issued_mfma(mode, big):
+    """MFMA type and dense peak (TFLOP/s) each GEMM's kernel issues, as
+    ((gate/up type, peak), (down type, peak)).  FP8 layers: the tiled
+    (many-token) kernels use the FP8 MFMA for both projections; the
+    few-token kernels widen the gate/up codes to bf16 and use the bf16 MFMA
+    (as fast there, where weights stream from HBM), the FP8 MFMA for the
+    down projection."""
+    if mode == 2:
+        return (("fp8e4m3", 5000.0) if big else ("bf16 (e4m3 codes widened)", 2500.0),
+                ("fp8e4m3", 5000.0))
+    return ((DTYPE_NAME[mode], MFMA_PEAK_TFLOPS[mode]),) * 2
+
 METRIC = "fused-MoE layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8e4m3"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -286,7 +296,7 @@ def measure(name, args, H_, full):
 
     active, layer_bytes, flops, w13_bytes, w13_flops = algorithmic(spec, counts)
     peak = MFMA_PEAK_TFLOPS[mode]
-    peak13, peak2 = ISSUED_PEAK_TFLOPS[mode]
+    (type13, peak13), (_, peak2) = issued_mfma(mode, lay.big)
     issued_roof_ms = (w13_flops / (peak13 * 1e12) + (flops - w13_flops) / (peak2 * 1e12)) * 1e3
     w13_gbs = w13_bytes / (w13_ms * 1e-3) / 1e9
     w13_tflops = w13_flops / (w13_ms * 1e-3) / 1e12
@@ -301,7 +311,7 @@ def measure(name, args, H_, full):
                 "traffic": traffic_for(spec.name, lay.kernel, kernel_sources(lay.big)),
                 "bytes_per_launch": w13_bytes, "flops_per_launch": w13_flops, "avg_ms": w13_ms,
                 "hbm_gbs": w13_gbs, "mfma_tflops": w13_tflops, "mfma_peak_tflops": peak,
-                "mfma_issued": "bf16 (e4m3 codes widened)" if mode == 2 else DTYPE_NAME[mode],
+                "mfma_issued": type13,
                 "mfma_frac_of_issued_type_peak": w13_tflops / peak13}
     rec = {
         "workload": "%s: T=%d H=%d E=%d k=%d I=%d" % (spec.name, spec.T, spec.H, spec.E, spec.k,
@@ -316,6 +326,7 @@ def measure(name, args, H_, full):
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / peak,
         "layer_mfma_frac_issued": issued_roof_ms / ms,
+        "mfma_types": {"gate_up": type13, "down": issued_mfma(mode, lay.big)[1][0]},
         "layer_alg_bytes": layer_bytes,
         "layer_alg_flops": flops,
         "roofline": roofline,
@@ -535,11 +546,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[spec.mode],
-        # the MFMA arithmetic of each GEMM (FP8 mode stores e4m3 weights and
-        # activations; its gate/up products run on the bf16 MFMA, exact for
-        # e4m3 values, its down projection on the FP8 MFMA)
-        "mfma_types": {"gate_up": "bf16 (e4m3 codes widened)" if spec.mode == 2 else
-                       DTYPE_NAME[spec.mode], "down": DTYPE_NAME[spec.mode]},
+        # the MFMA arithmetic each GEMM issues
+        "mfma_types": main_rec["mfma_types"],
         "data": "synthetic (seeded; moe_workloads recipe)",
         "config": {"workload": main_rec["workload"], "T": spec.T, "H": spec.H, "E": spec.E,
                    "k": spec.k, "I": spec.I, "active_experts": main_rec["active_experts"]},

@@ -30,19 +30,11 @@
 // rows counted over two 128-byte bank rows, so neither the stores nor the
 // MFMA fragment reads conflict in the LDS banks.
 //
-// FP8 gate/up projection (kFp8ViaBf16): the token stage is widened to bf16
-// as it is written to LDS and the weight fragments are widened in registers;
-// the products then go through the bf16 MFMA, whose sums are exact where the
-// FP8 MFMA's are not.  A widened row has 16 chunks of 16 bytes (chunk q
-// holding K values 8q .. 8q+7), kept as two planes with the geometry of an
-// FP8 stage: plane q & 1 (the odd chunks BM * 128 bytes after the even
-// ones), 128-byte rows, chunk q at slot (q >> 1) ^ swz(r).  A thread staging
-// FP8 chunk c of a row stores its bf16 chunks 2c and 2c+1 at slot c ^ swz(r)
-// of the two planes, and MFMA u of lane group g reads chunk 4g + u: plane
-// u & 1, slot (2g + u/2) ^ swz(r) -- the FP8 stage's store and fragment
-// patterns, whose 16-byte LDS accesses were measured free of bank conflicts
-// on gfx950 (a single 256-byte-row layout measured 2-way conflicts on both
-// its stores and its fragment reads).
+// In FP8 mode both projections run on the FP8 MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales): the many-token
+// layers are bound by MFMA issue as much as by HBM, and the FP8 instruction
+// does a 128-deep step in one issue where the bf16 one needs four.  Its
+// fp32 sums carry the instruction's own rounding.
 //
 // Launch order: block b takes tile b / NB and weight-row block b % NB, with
 // NB = (rows of the weight matrix) / (128*WN).  Blocks are dealt to the 8 XCDs
@@ -100,17 +92,15 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 // LDS bytes of one token-stage buffer.
 template <int MODE, int BM>
 constexpr int stage_lds_bytes() {
-  return BM * kStageB * (MODE == kFp8ViaBf16 ? 2 : 1);
+  return BM * kStageB;
 }
 
 template <int MODE, int BM, int WN, int PD, int MTA>
 __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const char* const* b_rows,
                                               int n_stages, char* lds, f32x4 (*acc)[MTA]) {
   static_assert(BM / 16 <= MTA && (BM % (32 * WN) == 0 || BM == 16 * WN), "tile shape");
-  constexpr bool VIA = MODE == kFp8ViaBf16;
-  typedef TileMma<VIA ? MOE_FP8_E4M3 : MODE> M;
-  constexpr int ROWB = kStageB;        // LDS bytes per token row (per plane when widened)
-  constexpr int PLANE = BM * kStageB;  // widened: the odd bf16 chunks' plane follows
+  typedef TileMma<MODE> M;
+  constexpr int ROWB = kStageB;  // LDS bytes per token row
   constexpr int B_BYTES = stage_lds_bytes<MODE, BM>();
   // token rows staged per thread; a stage of fewer than 32*WN rows is staged
   // by the threads with r0 < BM only (whole waves)
@@ -123,24 +113,16 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   const int c = t & 7, r0 = t >> 3;
   const int ca0 = M::chunk(g, 0) * 16, ca1 = M::chunk(g, 1) * 16;
 
-  int b_slot[NB], b_slot2[NB];
+  int b_slot[NB];
 #pragma unroll
   for (int i = 0; i < NB; i++) {
     const int r = r0 + 32 * WN * i;
     b_slot[i] = r * ROWB + ((c ^ swz(r)) << 4);
-    b_slot2[i] = VIA ? PLANE + b_slot[i] : 0;  // widened: bf16 chunks 2c and 2c+1
   }
   auto stage_b = [&](char* buf, const i32x4* src) {
     if (!ALL_STAGE && r0 >= BM) return;
 #pragma unroll
-    for (int i = 0; i < NB; i++) {
-      if (VIA) {
-        *reinterpret_cast<i32x4*>(buf + b_slot[i]) = e4m3x8_to_bf16x8(src[i][0], src[i][1]);
-        *reinterpret_cast<i32x4*>(buf + b_slot2[i]) = e4m3x8_to_bf16x8(src[i][2], src[i][3]);
-      } else {
-        *reinterpret_cast<i32x4*>(buf + b_slot[i]) = src[i];
-      }
-    }
+    for (int i = 0; i < NB; i++) *reinterpret_cast<i32x4*>(buf + b_slot[i]) = src[i];
   };
   // LDS offsets of this lane's two chunks in column tile j: row j*16 + r16,
   // whose swizzle is (r16 ^ (2j + r16 / 8)) & 7.
@@ -191,49 +173,28 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       load_b(min(kt + PD, last), rb[(q + PD) % RING]);
       // keeps this stage's MFMAs and the consumers of the stages in flight
       // from being scheduled up against the loads just issued (measured: FP8
-      // down projection 1.5% faster; the widening gate/up loop runs better
-      // with the compiler's own interleaving)
-      if constexpr (!VIA) __builtin_amdgcn_sched_barrier(0);
+      // down projection 1.5% faster)
+      __builtin_amdgcn_sched_barrier(0);
       const bool valid = kt < n_stages;
       const i32x8 a0 = valid ? ra[q][0] : zero8;
       const i32x8 a1 = valid ? ra[q][1] : zero8;
       const char* cur = lds + (kt & 1) * B_BYTES;
-      // the non-widening loop raises its wave priority over its MFMA burst
-      // (16k-token FP8 down projection 2% faster; the widening loop slower)
-      if constexpr (!VIA) __builtin_amdgcn_s_setprio(1);
-      if (VIA) {
-        // MFMA u: the lane's codes 8u .. 8u+7 of its 32 (K values
-        // 32g + 8u ..), i.e. bf16 chunk 4g + u of the token row
+      // the wave's priority is raised over its MFMA burst (16k-token FP8
+      // down projection 2% faster)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const bf16x8 a0u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a0[2 * u], a0[2 * u + 1]));
-          const bf16x8 a1u = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(a1[2 * u], a1[2 * u + 1]));
-          const char* plane = cur + (u & 1) * PLANE + b_base;
-#pragma unroll
-          for (int j = 0; j < MT; j++) {
-            const int sw = (r16 ^ (2 * j + r16h)) & 7;
-            const bf16x8 fb = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const i32x4*>(plane + j * 16 * ROWB +
-                                                        (((2 * g + (u >> 1)) ^ sw) << 4)));
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0u, fb, acc[0][j], 0, 0, 0);
-            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1u, fb, acc[1][j], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < MT; j++) {
-          const int sw = (r16 ^ (2 * j + r16h)) & 7;
-          const char* rowp = cur + j * 16 * kStageB + b_base;
-          const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
-                                *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
-          acc[0][j] = M::mma(a0, fb, acc[0][j]);
-          acc[1][j] = M::mma(a1, fb, acc[1][j]);
-        }
+      for (int j = 0; j < MT; j++) {
+        const int sw = (r16 ^ (2 * j + r16h)) & 7;
+        const char* rowp = cur + j * 16 * kStageB + b_base;
+        const i32x8 fb = join(*reinterpret_cast<const i32x4*>(rowp + ((cb0 ^ sw) << 4)),
+                              *reinterpret_cast<const i32x4*>(rowp + ((cb1 ^ sw) << 4)));
+        acc[0][j] = M::mma(a0, fb, acc[0][j]);
+        acc[1][j] = M::mma(a1, fb, acc[1][j]);
       }
-      if constexpr (!VIA) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
       // the token chunk of stage kt+1 (ring slot (q+1) % RING) into the
       // other LDS buffer
-      if constexpr (!VIA) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
       stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % RING]);
       __syncthreads();
     }
@@ -474,9 +435,9 @@ hipError_t launch_w13_tiles(int mode, int bm, const void* b, const void* w13,
   else if (mode == MOE_BF16 && bm == 128)
     MOE_W13_TILES(MOE_BF16, 128);
   else if (mode == MOE_FP8_E4M3 && bm == 64)
-    MOE_W13_TILES(kFp8ViaBf16, 64);
+    MOE_W13_TILES(MOE_FP8_E4M3, 64);
   else if (mode == MOE_FP8_E4M3 && bm == 128)
-    MOE_W13_TILES(kFp8ViaBf16, 128);
+    MOE_W13_TILES(MOE_FP8_E4M3, 128);
   else
     return hipErrorInvalidValue;
 #undef MOE_W13_TILES

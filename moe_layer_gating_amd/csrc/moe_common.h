@@ -38,8 +38,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // bf16 MFMA sums these products in fp32 (bit-equal to the rounded exact sum
 // 99% of the time, measured); the FP8 MFMA keeps fewer bits (about 2^-19 of
 // sum|p| per instruction, measured), and its error flips rounding decisions
-// made on the result.  Used for the gate/up projection, whose output is
-// rounded to bf16 and then quantised.
+// made on the result (about 2% of h's bf16 values).  Used for the gate/up
+// projection of the few-token kernels, which stream weights from HBM: there
+// the four bf16 MFMAs per 128-code step were measured as fast as one FP8
+// MFMA.  The many-token tiled kernels, bound by MFMA issue, take the FP8
+// MFMA for both projections.
 constexpr int kFp8ViaBf16 = 3;
 __host__ __device__ constexpr bool is_fp8(int mode) {
   return mode == MOE_FP8_E4M3 || mode == kFp8ViaBf16;

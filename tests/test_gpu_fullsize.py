@@ -34,7 +34,7 @@ import moe_layer_gating_amd as moe
 import moe_workloads as wl
 import oracle
 from gpu_helpers import (BF16, FP8, OUT_TOL, act_to_numpy, assert_grouping, bf16_step_ratio,
-                         fused_call, int_tensor, rel_inf, say, upload)
+                         fused_call, h_identical_min, int_tensor, rel_inf, say, upload)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -163,7 +163,7 @@ def test_prefill_fp8_full_sampled(name):
     ratio = bf16_step_ratio(hv[pos], oracle.to_f64(href, FP8))
     say("  sampled h: step ratio %.3f, identical %.4f" % (ratio, np.mean(hg[pos] == href)))
     assert ratio <= 1.0
-    assert np.mean(hg[pos] == href) > 0.99
+    assert np.mean(hg[pos] == href) >= h_identical_min(FP8, s.T, s.k, s.E)
     # down projection and aggregation of sampled tokens at full size, from
     # the GPU's own h (the e4m3 codes of h are decided on it, with the scale
     # of its amax, checked above): tokens of the heaviest expert's first and

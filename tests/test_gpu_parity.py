@@ -11,10 +11,10 @@ per-mode tolerance on max|gpu - ref| / max|ref| (fp32 1e-5, bf16 5e-3, FP8
 output type (both sides rounding to bf16 could otherwise differ by one
 output ulp, up to 2^-7 of max|ref|, for results that are both correct).
 Stage bars are tighter: h within one bf16 step of the oracle (see
-gpu_helpers.bf16_step_ratio) and at least 99% of its bf16 values identical
-(the FP8 gate/up products go through the bf16 MFMA on widened codes, which
-sums them exactly); y (fp32) within 1e-5, except FP8 where the down
-projection's FP8 MFMA rounds its sums (about 2^-19 of sum|p| per
+gpu_helpers.bf16_step_ratio) and at least 99% of its bf16 values identical,
+95% in the tiled FP8 kernels, whose gate/up products go through the FP8
+MFMA (gpu_helpers.h_identical_min); y (fp32) within 1e-5, except FP8 where
+the down projection's FP8 MFMA rounds its sums (about 2^-19 of sum|p| per
 instruction, measured) and the bar is 2e-4.
 Each stage is fed the oracle's upstream outputs so a failure names its stage.
 """
@@ -26,8 +26,8 @@ import moe_layer_gating_amd as moe
 import moe_workloads as wl
 import oracle
 from gpu_helpers import (BF16, F32, FP8, OUT_TOL, act_to_numpy, act_to_torch, assert_grouping,
-                         bf16_step_ratio, f32_tensor, fused_call, int_tensor, rel_inf, say,
-                         upload)
+                         bf16_step_ratio, f32_tensor, fused_call, h_identical_min, int_tensor,
+                         rel_inf, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,7 @@ def test_w13_swiglu(c):
         # every element within one bf16 step of the oracle's (see
         # bf16_step_ratio), almost all equal
         assert bf16_step_ratio(hv, rv) <= 1.0
-        assert np.mean(hg == ref["h"]) > 0.99
+        assert np.mean(hg == ref["h"]) >= h_identical_min(mode, c[1], k, c[3])
     if mode == FP8:
         s = sc.cpu().numpy()
         _, s_x, _ = oracle.act_quant(L["x"], BF16)
@@ -435,7 +435,7 @@ def test_planted_tile_edges(c):
     torch.cuda.synchronize()
     hg = act_to_numpy(h, mode)
     assert bf16_step_ratio(oracle.to_f64(hg, mode), oracle.to_f64(ref["h"], mode)) <= 1.0
-    assert np.mean(hg == ref["h"]) > 0.99
+    assert np.mean(hg == ref["h"]) >= h_identical_min(mode, T, k, E)
     act = np.zeros(4, np.float32)
     if mode == FP8:
         _, s_h, _ = oracle.act_quant(ref["h"], BF16)
