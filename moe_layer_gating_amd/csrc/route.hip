@@ -28,9 +28,20 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 }
 
 // LDS words of the per-wave scratch of gate_token's rank selection: the
-// token's logits (2 per lane), then k slot values and k slot experts.
+// token's selection keys (two 64-bit keys per lane), then k slot values and
+// k slot experts.
 constexpr int kRankMaxE = 2 * kWave;
-constexpr int kGateScratch = kRankMaxE + 2 * 16;
+constexpr int kGateScratch = 2 * kRankMaxE + 2 * 16;
+
+// Selection key of expert e with logit v: larger key = earlier in the order
+// (logit descending, expert index ascending).  The high word maps the float
+// to an unsigned integer of the same order (-0 first made +0, so the two
+// zeros tie as they compare equal), the low word is ~e.
+__device__ __forceinline__ uint64_t gate_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~e;
+}
 
 // Orders this wave's LDS accesses: every lane's earlier LDS writes are
 // complete and visible to the other lanes before any later access.
@@ -42,12 +53,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Top-k of one token by one whole wave; lanes 0..k-1 write slot `lane` to
 // ids_row / wts_row (and to lds_ids if given).  With `scratch` (kGateScratch
-// words of LDS owned by this wave) and E <= kRankMaxE the selection is by
-// ranks: the row goes to LDS and every lane counts, for each of its (at most
-// two) logits, the experts ordered before it by (logit desc, index asc),
-// reading the row back four logits at a time (broadcast reads); the logit of
-// rank j < k is slot j.  That is one pass of independent comparisons instead
-// of k dependent wave-wide arg-max rounds, and selects the same experts.
+// words of LDS owned by this wave, 8-byte aligned) and E <= kRankMaxE the
+// selection is by ranks: the selection keys of the row (gate_key) go to LDS
+// and every lane counts, for each of its (one, or two when E > 64) logits,
+// the keys larger than its own, reading them back two at a time (broadcast
+// reads); the logit of rank j < k is slot j.  That is one pass of
+// independent 64-bit comparisons instead of k dependent wave-wide arg-max
+// rounds, and selects the same experts.
 __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E, int k, int renorm,
                                            int32_t* __restrict__ ids_row,
                                            float* __restrict__ wts_row, int* lds_ids,
@@ -73,24 +85,42 @@ __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E,
   float my_v = -INFINITY, top_v = 0.f;
   int my_e = 0;
   if (scratch && E <= kRankMaxE) {
-    float* srow = scratch;
-    float* sv = scratch + kRankMaxE;
-    int* se = reinterpret_cast<int*>(scratch + kRankMaxE + 16);
+    uint64_t* skey = reinterpret_cast<uint64_t*>(scratch);
+    float* sv = scratch + 2 * kRankMaxE;
+    int* se = reinterpret_cast<int*>(scratch + 2 * kRankMaxE + 16);
     wave_lds_sync();  // a previous token's reads of this scratch are done
-    // v[i] is -inf beyond E: such an entry has an index >= E, so it never
-    // ranks before a real expert, and its own rank is at least E >= k
-    srow[lane] = v[0];
-    srow[lane + kWave] = v[1];
+    // v[i] is -inf beyond E: such an entry has an index >= E, so its key is
+    // below every real expert's, and its own rank is at least E >= k
+    const uint64_t k0 = gate_key(v[0], lane), k1 = gate_key(v[1], lane + kWave);
+    skey[lane] = k0;
+    skey[lane + kWave] = k1;
     wave_lds_sync();
     int r0 = 0, r1 = 0;
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(srow);
-    for (int q = 0; q < (E + 3) / 4; q++) {
-      const f32x4 c = s4[q];
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    const u64x2* s2 = reinterpret_cast<const u64x2*>(skey);
+    // eight 16-byte reads per round; rounds past E read the padding keys
+    // (all kRankMaxE are written), which never exceed a real expert's key
+    const int nq = (E + 1) / 2;
+    if (E > kWave) {
+      for (int q0 = 0; q0 < nq; q0 += 8) {
+        u64x2 c[8];
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        r0 += better(c[u], 4 * q + u, v[0], lane);
-        r1 += better(c[u], 4 * q + u, v[1], lane + kWave);
+        for (int u = 0; u < 8; u++) c[u] = s2[q0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          r0 += (c[u][0] > k0) + (c[u][1] > k0);
+          r1 += (c[u][0] > k1) + (c[u][1] > k1);
+        }
       }
+    } else {
+      for (int q0 = 0; q0 < nq; q0 += 8) {
+        u64x2 c[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) c[u] = s2[q0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; u++) r0 += (c[u][0] > k0) + (c[u][1] > k0);
+      }
+      r1 = kRankMaxE;  // the second slot is padding
     }
     if (lane < E && r0 < k) {
       sv[r0] = v[0];
@@ -162,12 +192,13 @@ __global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restric
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ wts,
                                                           uint32_t* zero_words, int n_zero) {
+  __shared__ __attribute__((aligned(16))) float gscr[4][kGateScratch];
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   gate_token(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k,
-             nullptr);
+             nullptr, gscr[threadIdx.x / kWave]);
 }
 
 hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
