@@ -559,9 +559,28 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     __syncthreads();
     const int cnt = (t < E) ? hist[t] : 0;
     const int nt = (cnt + bm - 1) / bm;
-    int total_pairs, total_tiles;
-    const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
-    const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
+    // one scan of both counts packed in one int (each total is at most
+    // kRouteSmallMax < 2^16); with E <= 64 every expert is in wave 0, whose
+    // shuffle scan alone then suffices (the totals are read by thread 0)
+    static_assert(kRouteSmallMax < (1 << 16), "packed scan");
+    const int packed = cnt | (nt << 16);
+    int ptot = 0, ppre = 0;
+    if (E <= kWave) {
+      if (w == 0) {
+        int incl = packed;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int nb = __shfl_up(incl, o);
+          if (lane >= o) incl += nb;
+        }
+        ppre = incl - packed;
+        ptot = __shfl(incl, kWave - 1);
+      }
+    } else {
+      ppre = block_exclusive_scan_1024(packed, tmp, &ptot);
+    }
+    const int pre = ppre & 0xffff, tpre = ppre >> 16;
+    const int total_tiles = ptot >> 16;
     if (t < E) {
       counts[t] = cnt;
       offsets[t] = pre;
