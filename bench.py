@@ -42,7 +42,8 @@ Prints ONE JSON line with tokens/s as `value`, plus:
                   separate figure;
   flushed      -- single calls timed alone (event pair around each call) after
                   reading a 1 GiB buffer that evicts L2 and the 256 MB MALL:
-                  median, p10 and p90, as a separate figure;
+                  median, p10 and p90 over 100 calls (few-token layers) or 20
+                  (tiled layers), as a separate figure;
   router       -- the layer run from the router weights instead of the logits
                   (moe_fused_forward_router: for few-token bf16/FP8 batches
                   the front kernel computes the logits itself, one launch
@@ -381,7 +382,8 @@ def measure(name, args, H_, full):
         # single calls after an L2 / MALL flush (outside the timed region):
         # the flush only reads, so the timed call inherits no dirty lines
         flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        fpairs = [(new_event(), new_event()) for _ in range(min(args.steps, 20))]
+        # 100 calls for the few-token (decode) layers, 20 for the tiled ones
+        fpairs = [(new_event(), new_event()) for _ in range(20 if lay.big else 100)]
         for a, b in fpairs:
             flush_buf.sum()
             lay.step([a, None, None, None, None, None, None, None, b])
