@@ -34,8 +34,10 @@ namespace moe {
 // thread per unit, so each value and each table entry is loaded once.
 // Interleaved pairing: one thread per chunk (its pairs lie inside it).  A
 // head's units occupy G = next power of two lanes, so its amax is a
-// butterfly over G lanes.
-template <bool INTER>
+// butterfly over G lanes.  A thread takes the same unit of HPT consecutive
+// heads of one token (HPT divides the head count): the token's table entries
+// are loaded once for all of them, and HPT heads' loads are in flight.
+template <bool INTER, int HPT>
 __global__ __launch_bounds__(256) void inv_rope_fp8_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ positions,
     const float* __restrict__ cos_sin, long n_heads_total, int n_heads, int head_dim, int rot_dim,
@@ -47,81 +49,123 @@ __global__ __launch_bounds__(256) void inv_rope_fp8_kernel(
 #pragma clang fp contract(off)
   const int lane = lane_id();
   const int u = lane & (G - 1);  // work unit of the head
-  const long th = ((long)blockIdx.x * blockDim.x + threadIdx.x) / G;
+  const long hg = ((long)blockIdx.x * blockDim.x + threadIdx.x) / G;  // group of HPT heads
   const int half = rot_dim / 2;
   const int h8 = rot_dim / 16;  // chunk pairs (rotate half)
   const int units = INTER ? head_dim / 8 : h8 + (head_dim - rot_dim) / 8;
-  const bool live = th < n_heads_total && u < units;
+  const bool live = hg * HPT < n_heads_total && u < units;
   // chunk c0 holds y[0..8); rotate-half pair units also chunk c1 = c0 + h8
   // with y[8..16)
   const int c0 = INTER || u < h8 ? u : u + h8;
   const bool pair = !INTER && u < h8;
-  float y[16];
-  float m = 0.f;
+  float y[HPT][16];
+  float m[HPT];
+#pragma unroll
+  for (int hh = 0; hh < HPT; hh++) m[hh] = 0.f;
   if (live) {
-    const long t = th / n_heads;
+    const long th0 = hg * HPT;
+    const long t = th0 / n_heads;
     int p = positions[t];
     p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
     const float* cs = cos_sin + (size_t)p * rot_dim;
-    const uint16_t* xh = x + (size_t)th * head_dim;
-    const i32x4 v0 = *reinterpret_cast<const i32x4*>(xh + 8 * c0);
-    const i32x4 v1 = pair ? *reinterpret_cast<const i32x4*>(xh + 8 * (c0 + h8)) : v0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      y[2 * j] = bf16_to_f32((uint16_t)((uint32_t)v0[j] & 0xffffu));
-      y[2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v0[j] >> 16));
-      y[8 + 2 * j] = bf16_to_f32((uint16_t)((uint32_t)v1[j] & 0xffffu));
-      y[8 + 2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v1[j] >> 16));
-    }
+    // the unit's table entries: cosines then sines of its 4 (interleaved)
+    // or 8 (rotate half) pairs
+    float cv[8], sv[8];
     if (INTER) {
-      if (8 * c0 < rot_dim) {  // pairs (2i, 2i+1), i = 4 c0 + j
+      if (8 * c0 < rot_dim) {
         const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * c0);
         const f32x4 s = *reinterpret_cast<const f32x4*>(cs + half + 4 * c0);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const float xa = y[2 * j], xb = y[2 * j + 1];
-          y[2 * j] = xa * c[j] + xb * s[j];
-          y[2 * j + 1] = xb * c[j] - xa * s[j];
+          cv[j] = c[j];
+          sv[j] = s[j];
         }
       }
-    } else if (pair) {  // pairs (8 c0 + j, 8 c0 + j + half)
+    } else if (pair) {
       const f32x4 ca = *reinterpret_cast<const f32x4*>(cs + 8 * c0);
       const f32x4 cb = *reinterpret_cast<const f32x4*>(cs + 8 * c0 + 4);
       const f32x4 sa = *reinterpret_cast<const f32x4*>(cs + half + 8 * c0);
       const f32x4 sb = *reinterpret_cast<const f32x4*>(cs + half + 8 * c0 + 4);
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float c = j < 4 ? ca[j] : cb[j - 4], s = j < 4 ? sa[j] : sb[j - 4];
-        const float xa = y[j], xb = y[8 + j];
-        y[j] = xa * c + xb * s;
-        y[8 + j] = xb * c - xa * s;
+      for (int j = 0; j < 4; j++) {
+        cv[j] = ca[j];
+        cv[4 + j] = cb[j];
+        sv[j] = sa[j];
+        sv[4 + j] = sb[j];
       }
     }
+    i32x4 v0[HPT], v1[HPT];
 #pragma unroll
-    for (int j = 0; j < 16; j++)
-      if (j < 8 || pair) m = fmaxf(m, fabsf(y[j]));
+    for (int hh = 0; hh < HPT; hh++) {
+      const uint16_t* xh = x + (size_t)(th0 + hh) * head_dim;
+      v0[hh] = *reinterpret_cast<const i32x4*>(xh + 8 * c0);
+      if (pair) v1[hh] = *reinterpret_cast<const i32x4*>(xh + 8 * (c0 + h8));
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPT; hh++) {
+      float* yh = y[hh];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        yh[2 * j] = bf16_to_f32((uint16_t)((uint32_t)v0[hh][j] & 0xffffu));
+        yh[2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v0[hh][j] >> 16));
+        if (pair) {
+          yh[8 + 2 * j] = bf16_to_f32((uint16_t)((uint32_t)v1[hh][j] & 0xffffu));
+          yh[8 + 2 * j + 1] = bf16_to_f32((uint16_t)((uint32_t)v1[hh][j] >> 16));
+        }
+      }
+      if (INTER) {
+        if (8 * c0 < rot_dim) {  // pairs (2i, 2i+1), i = 4 c0 + j
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float xa = yh[2 * j], xb = yh[2 * j + 1];
+            yh[2 * j] = xa * cv[j] + xb * sv[j];
+            yh[2 * j + 1] = xb * cv[j] - xa * sv[j];
+          }
+        }
+      } else if (pair) {  // pairs (8 c0 + j, 8 c0 + j + half)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const float xa = yh[j], xb = yh[8 + j];
+          yh[j] = xa * cv[j] + xb * sv[j];
+          yh[8 + j] = xb * cv[j] - xa * sv[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j++)
+        if (j < 8 || pair) m[hh] = fmaxf(m[hh], fabsf(yh[j]));
+    }
   }
-  // amax over the head's G lanes (G divides 64; groups are lane-aligned)
-  for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // amax over each head's G lanes (G divides 64; groups are lane-aligned)
+#pragma unroll
+  for (int hh = 0; hh < HPT; hh++)
+    for (int o = 1; o < G; o <<= 1) m[hh] = fmaxf(m[hh], __shfl_xor(m[hh], o));
   if (!live) return;
-  const float sc = m > 0.f ? m / 448.0f : 1.0f;
-  const float r = m > 0.f ? 448.0f / m : 1.0f;
-  uint8_t* ch = codes + (size_t)th * head_dim;
 #pragma unroll
-  for (int k8 = 0; k8 < 2; k8++) {
-    if (k8 == 1 && !pair) break;
-    float f[8];
+  for (int hh = 0; hh < HPT; hh++) {
+    const long th = hg * HPT + hh;
+    const float sc = m[hh] > 0.f ? m[hh] / 448.0f : 1.0f;
+    const float r = m[hh] > 0.f ? 448.0f / m[hh] : 1.0f;
+    uint8_t* ch = codes + (size_t)th * head_dim;
 #pragma unroll
-    for (int j = 0; j < 8; j++)
-      f[j] = __builtin_amdgcn_fmed3f(y[8 * k8 + j] * r, -448.0f, 448.0f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-    *reinterpret_cast<uint2*>(ch + 8 * (c0 + k8 * h8)) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    for (int k8 = 0; k8 < 2; k8++) {
+      if (k8 == 1 && !pair) break;
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        f[j] = __builtin_amdgcn_fmed3f(y[hh][8 * k8 + j] * r, -448.0f, 448.0f);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+      *reinterpret_cast<uint2*>(ch + 8 * (c0 + k8 * h8)) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    }
+    if (u == 0) scales[th] = sc;
   }
-  if (u == 0) scales[th] = sc;
 }
+
+// Heads per thread: 4 when the head count allows it and the batch still
+// gives every CU several blocks, else 1.
+constexpr long kRopeMultiHeadMin = 16384;  // heads
 
 hipError_t launch_inv_rope_fp8(const uint16_t* x, const int32_t* positions, const float* cos_sin,
                                int T, int n_heads, int head_dim, int rot_dim, int max_pos,
@@ -131,15 +175,26 @@ hipError_t launch_inv_rope_fp8(const uint16_t* x, const int32_t* positions, cons
   while (G < units) G <<= 1;
   if (G > kWave) return hipErrorInvalidValue;
   const long heads = (long)T * n_heads;
-  const long threads = heads * G;
+  const int hpt = (n_heads % 4 == 0 && heads >= kRopeMultiHeadMin) ? 4 : 1;
+  const long threads = heads / hpt * G;
   const long grid = (threads + 255) / 256;
   if (grid <= 0) return hipSuccess;
-  if (interleaved)
-    inv_rope_fp8_kernel<true><<<grid, 256, 0, st>>>(x, positions, cos_sin, heads, n_heads,
-                                                    head_dim, rot_dim, max_pos, G, codes, scales);
-  else
-    inv_rope_fp8_kernel<false><<<grid, 256, 0, st>>>(x, positions, cos_sin, heads, n_heads,
-                                                     head_dim, rot_dim, max_pos, G, codes, scales);
+#define MOE_ROPE(INTER_, HPT_)                                                              \
+  inv_rope_fp8_kernel<INTER_, HPT_><<<grid, 256, 0, st>>>(x, positions, cos_sin, heads, n_heads, \
+                                                          head_dim, rot_dim, max_pos, G, codes,  \
+                                                          scales)
+  if (interleaved) {
+    if (hpt == 4)
+      MOE_ROPE(true, 4);
+    else
+      MOE_ROPE(true, 1);
+  } else {
+    if (hpt == 4)
+      MOE_ROPE(false, 4);
+    else
+      MOE_ROPE(false, 1);
+  }
+#undef MOE_ROPE
   return hipGetLastError();
 }
 
