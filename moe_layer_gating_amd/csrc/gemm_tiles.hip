@@ -16,12 +16,22 @@
 // to the fp32 accumulators in the epilogue (agentic-affairs.com, "Triton
 // improves the FP8 execution path").
 //
-// Weights are streamed from HBM straight into registers in MFMA operand
-// layout (no LDS round trip: every weight byte is used by exactly one wave),
-// prefetched kPD stages ahead through a ring of kPD + 1 register slots per
-// wave.  The token tile is shared by the block's waves: it is prefetched into
-// registers the same way and written to a double-buffered LDS tile one stage
-// before use.  Tiles holding at most a quarter or a half of BM positions run
+// Weights are streamed from HBM into registers with full-line loads (lane l
+// of load i reads 16-byte chunk l % 8 of the wave's row 8i + l / 8, so each
+// load instruction covers eight whole 128-byte lines), prefetched kPD stages
+// ahead through a ring of kPD + 1 register slots per wave.  The MFMA operand
+// layout wants 16 rows x 32 bytes per instruction instead (four lanes per
+// row): loaded that way, every instruction touches 16 half-used lines, and
+// L2-resident data then reached the CUs at a third of the full-line rate
+// (9.8 against 30.9 TB/s, measured).  So each stage passes through a
+// wave-private 4 KB LDS region: the ring slot is stored with the full-line
+// lane layout and read back in MFMA layout, chunk c of wave row r kept at
+// slot c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive lanes
+// (16 rows, one chunk index) fall on 16 distinct 16-byte bank groups.  The
+// MFMA operands and sums are those of the direct loads (bit-identical
+// results).  The token tile is shared by the block's waves: it is prefetched
+// into registers the same way and written to a double-buffered LDS tile one
+// stage before use.  Tiles holding at most a quarter or a half of BM positions run
 // a narrower copy of the main loop.
 //
 // LDS layout of a token stage: row r keeps its 16-byte chunk c at slot
@@ -85,7 +95,8 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 }
 
 // Main loop shared by both projections.
-//   a_rows[i]: this lane's weight row of the wave's row tile i (K offset 0);
+//   a_rows[i]: this lane's weight row of full-line load i, at its chunk
+//              (K offset 0);
 //   b_rows[i]: this thread's staged token rows r0 + 32*WN*i, already offset
 //              by the thread's chunk (t & 7) * 16;
 //   acc[i][j]: row tile i, column tile j of the wave's 32 x BM accumulator.
@@ -111,7 +122,6 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   const int lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int c = t & 7, r0 = t >> 3;
-  const int ca0 = M::chunk(g, 0) * 16, ca1 = M::chunk(g, 1) * 16;
 
   int b_slot[NB];
 #pragma unroll
@@ -128,6 +138,23 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   // whose swizzle is (r16 ^ (2j + r16 / 8)) & 7.
   const int b_base = r16 * ROWB;
   const int cb0 = M::chunk(g, 0), cb1 = M::chunk(g, 1), r16h = r16 >> 3;
+  // the wave's weight stage in LDS: 32 rows of 128 B, chunk c of wave row r
+  // at slot c ^ ((r >> 1) & 7); written from the full-line loads (lane l:
+  // row 8i + l / 8, chunk l % 8 of load i), read back in MFMA layout
+  char* wbuf = lds + 2 * B_BYTES + (t / kWave) * 4096;
+  int w_st[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 8 * i + (lane >> 3), cc = lane & 7;
+    w_st[i] = r * 128 + ((cc ^ ((r >> 1) & 7)) << 4);
+  }
+  int w_ld[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int r = 16 * i + r16;
+    w_ld[i][0] = r * 128 + ((cb0 ^ ((r >> 1) & 7)) << 4);
+    w_ld[i][1] = r * 128 + ((cb1 ^ ((r >> 1) & 7)) << 4);
+  }
 
   // Both operands are prefetched PD stages ahead: a wave's loads complete in
   // issue order, so waiting for a stage's token chunk also waits for every
@@ -139,12 +166,10 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   // clamped to the last stage (an overrun re-reads it), and the stages that
   // pad the final group of PD + 1 use zero weight fragments.
   const int last = n_stages - 1;
-  auto load_a = [&](int kt, i32x8* dst) {
+  auto load_a = [&](int kt, i32x4* dst) {
     const size_t off = (size_t)kt * kStageB;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-      dst[i] = join(*reinterpret_cast<const i32x4*>(a_rows[i] + off + ca0),
-                    *reinterpret_cast<const i32x4*>(a_rows[i] + off + ca1));
+    for (int i = 0; i < 4; i++) dst[i] = *reinterpret_cast<const i32x4*>(a_rows[i] + off);
   };
   auto load_b = [&](int kt, i32x4* dst) {
     if (!ALL_STAGE && r0 >= BM) return;
@@ -153,7 +178,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
     for (int i = 0; i < NB; i++) dst[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
   };
   constexpr int RING = PD + 1;
-  i32x8 ra[RING][2];
+  i32x4 ra[RING][4];
   i32x4 rb[RING][NB];
 #pragma unroll
   for (int p = 0; p < PD; p++) {
@@ -176,8 +201,16 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
       // down projection 1.5% faster)
       __builtin_amdgcn_sched_barrier(0);
       const bool valid = kt < n_stages;
-      const i32x8 a0 = valid ? ra[q][0] : zero8;
-      const i32x8 a1 = valid ? ra[q][1] : zero8;
+      // weights of this stage through the wave's LDS region into MFMA layout
+#pragma unroll
+      for (int i = 0; i < 4; i++) *reinterpret_cast<i32x4*>(wbuf + w_st[i]) = ra[q][i];
+      i32x8 af[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+        af[i] = join(*reinterpret_cast<const i32x4*>(wbuf + w_ld[i][0]),
+                     *reinterpret_cast<const i32x4*>(wbuf + w_ld[i][1]));
+      const i32x8 a0 = valid ? af[0] : zero8;
+      const i32x8 a1 = valid ? af[1] : zero8;
       const char* cur = lds + (kt & 1) * B_BYTES;
       // the wave's priority is raised over its MFMA burst (16k-token FP8
       // down projection 2% faster)
@@ -239,7 +272,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
     void* __restrict__ h, uint32_t* amax_h_bits) {
   constexpr int ES = MODE == MOE_BF16 ? 2 : 1;
   constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * stage_lds_bytes<MODE, BM>()];
+  __shared__ __attribute__((aligned(16))) char lds[2 * stage_lds_bytes<MODE, BM>() + 4096 * 4 * WN];
   const int NBLK = 2 * I / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;
@@ -250,13 +283,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
   const int r16 = lane & 15, g = lane >> 4;
   const size_t row_bytes = (size_t)H * ES;
 
-  const char* a_rows[2];
+  // full-line weight loads: load i of lane l reads chunk l % 8 of the
+  // wave's row 8i + l / 8, i.e. MFMA row tile wr / 16, row wr % 16
+  const char* a_rows[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int q = 2 * w + i;
-    const int f = nb * 64 * WN + q * 8 + (r16 >> 1);
-    const int wrow = (r16 & 1) ? I + f : f;
-    a_rows[i] = w13 + ((size_t)tl.e * 2 * I + wrow) * row_bytes;
+  for (int i = 0; i < 4; i++) {
+    const int wr = 8 * i + (lane >> 3), rr = wr & 15;
+    const int q = 2 * w + (wr >> 4);
+    const int f = nb * 64 * WN + q * 8 + (rr >> 1);
+    const int wrow = (rr & 1) ? I + f : f;
+    a_rows[i] = w13 + ((size_t)tl.e * 2 * I + wrow) * row_bytes + (lane & 7) * 16;
   }
   const char* b_rows[BM / (32 * WN)];
 #pragma unroll
@@ -325,7 +361,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict_
                                                 void* __restrict__ y) {
   constexpr int ES = MODE == MOE_FP8_E4M3 ? 1 : 2;
   constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB];
+  __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB + 4096 * 4 * WN];
   const int NBLK = H / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;
@@ -336,10 +372,11 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict_
   const int r16 = lane & 15, g = lane >> 4;
   const size_t row_bytes = (size_t)I * ES;
 
-  const char* a_rows[2];
+  const char* a_rows[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
-    a_rows[i] = w2 + ((size_t)tl.e * H + nb * kTileN * WN + w * 32 + i * 16 + r16) * row_bytes;
+  for (int i = 0; i < 4; i++)
+    a_rows[i] = w2 + ((size_t)tl.e * H + nb * kTileN * WN + w * 32 + 8 * i + (lane >> 3)) *
+                         row_bytes + (lane & 7) * 16;
   const char* b_rows[BM / (32 * WN)];
 #pragma unroll
   for (int i = 0; i < BM / (32 * WN); i++) {
