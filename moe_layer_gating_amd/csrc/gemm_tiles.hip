@@ -30,9 +30,10 @@
 // (16 rows, one chunk index) fall on 16 distinct 16-byte bank groups.  The
 // MFMA operands and sums are those of the direct loads (bit-identical
 // results).  The token tile is shared by the block's waves: it is prefetched
-// into registers the same way and written to a double-buffered LDS tile one
-// stage before use.  Tiles holding at most a quarter or a half of BM positions run
-// a narrower copy of the main loop.
+// into registers the same way and written to one of four LDS stage buffers
+// two stages before use, with one barrier per two stages.  Tiles holding at
+// most a quarter or a half of BM positions run a narrower copy of the main
+// loop.
 //
 // LDS layout of a token stage: row r keeps its 16-byte chunk c at slot
 // c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7.  Eight consecutive rows read at
@@ -58,6 +59,7 @@ namespace moe {
 constexpr int kTileN = 128;  // weight rows per 4 waves
 constexpr int kStageB = 128;  // bytes of K per row per stage
 constexpr int kPD = 3;        // weight stages in flight per wave
+constexpr int kTokBufs = 4;   // LDS token-chunk buffers (stages)
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -141,7 +143,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   // the wave's weight stage in LDS: 32 rows of 128 B, chunk c of wave row r
   // at slot c ^ ((r >> 1) & 7); written from the full-line loads (lane l:
   // row 8i + l / 8, chunk l % 8 of load i), read back in MFMA layout
-  char* wbuf = lds + 2 * B_BYTES + (t / kWave) * 4096;
+  char* wbuf = lds + kTokBufs * B_BYTES + (t / kWave) * 4096;
   int w_st[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -156,16 +158,19 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
     w_ld[i][1] = r * 128 + ((cb1 ^ ((r >> 1) & 7)) << 4);
   }
 
-  // Both operands are prefetched PD stages ahead: a wave's loads complete in
-  // issue order, so waiting for a stage's token chunk also waits for every
-  // load issued before it, and a shorter token prefetch would drain the
-  // weight ring.  The ring has PD + 1 register slots, so the loads of stage
-  // kt+PD go into the slot stage kt-1 has freed and are issued before the
-  // MFMAs of stage kt, which then run while PD stages are in flight.
-  // Prefetch stage indices are clamped to the last stage (an overrun re-reads
-  // it), and the stages that pad the final group of PD + 1 skip their MFMAs
-  // by a block-uniform branch (244 VGPRs against the 256 that zero weight
-  // fragments took, and 1.5-2% faster).
+  // Weights are prefetched PD stages ahead, token chunks PD + 1 stages ahead,
+  // both through rings of PD + 1 register slots, and the loads of a stage go
+  // out before its MFMAs.  A token chunk is written to LDS two stages before
+  // use, into one of kTokBufs = 4 stage buffers, so one barrier per two
+  // stages both publishes the next two chunks and retires the two buffers
+  // just read (a barrier per stage cost 6-12% of the gate/up time).  A wave's
+  // loads complete in issue order, so each stage issues its token chunk
+  // before its weights: the wait for chunk s+2 at stage s then covers the
+  // weights of stage s only, never those of s+1.  Prefetch stage indices are
+  // clamped to the last stage (an overrun re-reads it), and the stages that
+  // pad the final group of PD + 1 skip their MFMAs by a block-uniform branch
+  // (fewer VGPRs than zero weight fragments, and 1.5-2% faster).
+  static_assert(PD == 3 && kTokBufs == 4, "prologue and ring written for PD = 3");
   const int last = n_stages - 1;
   auto load_a = [&](int kt, i32x4* dst) {
     const size_t off = (size_t)kt * kStageB;
@@ -179,14 +184,18 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
     for (int i = 0; i < NB; i++) dst[i] = *reinterpret_cast<const i32x4*>(b_rows[i] + off);
   };
   constexpr int RING = PD + 1;
-  i32x4 ra[RING][4];
-  i32x4 rb[RING][NB];
-#pragma unroll
-  for (int p = 0; p < PD; p++) {
-    load_a(min(p, last), ra[p]);
-    load_b(min(p, last), rb[p]);
-  }
+  i32x4 ra[RING][4];   // weights of stage s in slot s % RING
+  i32x4 rb[RING][NB];  // token chunk of stage s in slot s % RING
+  // chunks of stages 0-3 and weights of stages 0-2, chunk before weights
+  load_b(0, rb[0]);
+  load_b(min(1, last), rb[1]);
+  load_a(0, ra[0]);
+  load_b(min(2, last), rb[2]);
+  load_a(min(1, last), ra[1]);
+  load_b(min(3, last), rb[3]);
+  load_a(min(2, last), ra[2]);
   stage_b(lds, rb[0]);
+  stage_b(lds + B_BYTES, rb[1]);
   __syncthreads();
 
   const int n_groups = (n_stages + RING - 1) / RING;
@@ -194,8 +203,9 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
 #pragma unroll
     for (int q = 0; q < RING; q++) {
       const int kt = grp * RING + q;
+      // slot q held the chunk of stage kt, written to LDS two stages ago
+      load_b(min(kt + RING, last), rb[q]);
       load_a(min(kt + PD, last), ra[(q + PD) % RING]);
-      load_b(min(kt + PD, last), rb[(q + PD) % RING]);
       // keeps this stage's MFMAs and the consumers of the stages in flight
       // from being scheduled up against the loads just issued (measured: FP8
       // down projection 1.5% faster)
@@ -210,7 +220,7 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
         af[i] = join(*reinterpret_cast<const i32x4*>(wbuf + w_ld[i][0]),
                      *reinterpret_cast<const i32x4*>(wbuf + w_ld[i][1]));
       const i32x8 a0 = af[0], a1 = af[1];
-      const char* cur = lds + (kt & 1) * B_BYTES;
+      const char* cur = lds + q * B_BYTES;
       // the wave's priority is raised over its MFMA burst (16k-token FP8
       // down projection 2% faster)
       __builtin_amdgcn_s_setprio(1);
@@ -226,11 +236,11 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      // the token chunk of stage kt+1 (ring slot (q+1) % RING) into the
-      // other LDS buffer
+      // the token chunk of stage kt+2 into its LDS buffer, last read at
+      // stage kt-2 (before the previous barrier)
       __builtin_amdgcn_sched_barrier(0);
-      stage_b(lds + ((kt + 1) & 1) * B_BYTES, rb[(q + 1) % RING]);
-      __syncthreads();
+      stage_b(lds + ((q + 2) % RING) * B_BYTES, rb[(q + 2) % RING]);
+      if (q & 1) __syncthreads();
     }
   }
 }
@@ -273,7 +283,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w13_swiglu_tiles(
     void* __restrict__ h, uint32_t* amax_h_bits) {
   constexpr int ES = MODE == MOE_BF16 ? 2 : 1;
   constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * stage_lds_bytes<MODE, BM>() + 4096 * 4 * WN];
+  __shared__ __attribute__((aligned(16))) char lds[kTokBufs * stage_lds_bytes<MODE, BM>() +
+                                                    4096 * 4 * WN];
   const int NBLK = 2 * I / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;
@@ -362,7 +373,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w2_tiles(const char* __restrict_
                                                 void* __restrict__ y) {
   constexpr int ES = MODE == MOE_FP8_E4M3 ? 1 : 2;
   constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BM * kStageB + 4096 * 4 * WN];
+  __shared__ __attribute__((aligned(16))) char lds[kTokBufs * BM * kStageB + 4096 * 4 * WN];
   const int NBLK = H / (kTileN * WN);
   const int tile_idx = blockIdx.x / NBLK;
   const int nb = blockIdx.x - tile_idx * NBLK;

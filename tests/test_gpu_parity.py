@@ -55,6 +55,9 @@ CASES = [
     ("bf16_tiles_zipf", 256, 384, 16, 4, 384, BF16, "zipf"),
     ("fp8_tiles_empty", 256, 256, 16, 4, 640, FP8, "empty"),
     ("bf16_tiles_one_expert", 200, 256, 1, 1, 512, BF16, "uniform"),
+    # two experts with runs of dozens of 128-position tiles each (a skewed
+    # split, ragged last tiles, more tiles than one row block's XCD share)
+    ("fp8_tiles_long_runs", 9300, 128, 2, 1, 128, FP8, "zipf"),
     # 16 <= mean pairs per expert < 64: 64-position tiles, some experts spill
     # into a second tile
     ("fp8_tiles64_ragged", 250, 384, 8, 2, 384, FP8, "uniform"),
