@@ -26,8 +26,10 @@
 // (9.8 against 30.9 TB/s, measured).  So each stage passes through a
 // wave-private 4 KB LDS region: the ring slot is stored with the full-line
 // lane layout and read back in MFMA layout, chunk c of wave row r kept at
-// slot c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive lanes
-// (16 rows, one chunk index) fall on 16 distinct 16-byte bank groups.  The
+// slot c ^ swz(r) like the token tile below, so neither the stores nor the
+// fragment reads (16 rows at one chunk index) conflict in the LDS banks
+// (counters: 51 M conflict cycles per gate/up launch with slot
+// c ^ ((r >> 1) & 7), none with swz).  The
 // MFMA operands and sums are those of the direct loads (bit-identical
 // results).  The token tile is shared by the block's waves: it is prefetched
 // into registers the same way and written to one of four LDS stage buffers
@@ -141,21 +143,21 @@ __device__ __forceinline__ void tile_mainloop(const char* const* a_rows, const c
   const int b_base = r16 * ROWB;
   const int cb0 = M::chunk(g, 0), cb1 = M::chunk(g, 1), r16h = r16 >> 3;
   // the wave's weight stage in LDS: 32 rows of 128 B, chunk c of wave row r
-  // at slot c ^ ((r >> 1) & 7); written from the full-line loads (lane l:
+  // at slot c ^ swz(r); written from the full-line loads (lane l:
   // row 8i + l / 8, chunk l % 8 of load i), read back in MFMA layout
   char* wbuf = lds + kTokBufs * B_BYTES + (t / kWave) * 4096;
   int w_st[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int r = 8 * i + (lane >> 3), cc = lane & 7;
-    w_st[i] = r * 128 + ((cc ^ ((r >> 1) & 7)) << 4);
+    w_st[i] = r * 128 + ((cc ^ swz(r)) << 4);
   }
   int w_ld[2][2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int r = 16 * i + r16;
-    w_ld[i][0] = r * 128 + ((cb0 ^ ((r >> 1) & 7)) << 4);
-    w_ld[i][1] = r * 128 + ((cb1 ^ ((r >> 1) & 7)) << 4);
+    w_ld[i][0] = r * 128 + ((cb0 ^ swz(r)) << 4);
+    w_ld[i][1] = r * 128 + ((cb1 ^ swz(r)) << 4);
   }
 
   // Weights are prefetched PD stages ahead, token chunks PD + 1 stages ahead,
