@@ -62,6 +62,11 @@ CASES = [
     # two experts with runs of dozens of 128-position tiles each (a skewed
     # split, ragged last tiles, more tiles than one row block's XCD share)
     ("fp8_tiles_long_runs", 9300, 128, 2, 1, 128, FP8, "zipf"),
+    # 256 or more pairs per expert: many full 128-position tiles per expert,
+    # heavy skew, ragged last tiles of every width
+    ("fp8_tiles_heavy_zipf", 3000, 256, 8, 2, 256, FP8, "zipf"),
+    ("bf16_tiles_heavy", 2900, 256, 8, 1, 384, BF16, "uniform"),
+    ("fp8_tiles_heavy_h384", 1100, 384, 4, 1, 256, FP8, "uniform"),
     # 16 <= mean pairs per expert < 64: 64-position tiles, some experts spill
     # into a second tile
     ("fp8_tiles64_ragged", 250, 384, 8, 2, 384, FP8, "uniform"),
