@@ -48,9 +48,9 @@ CASES = [
     # (gating, grouping and tile-list kernels) instead of the one-block one
     ("fp8_skinny_many_pairs", 40, 256, 64, 8, 256, FP8, "uniform"),
     # few-token class at 48, 96 and 256 pairs (about 40, 65 and 20 tiles)
-    ("fp8_w2c_two_chunks", 6, 256, 64, 8, 256, FP8, "uniform"),
-    ("bf16_w2c_one_chunk", 12, 256, 128, 8, 256, BF16, "uniform"),
-    ("fp8_w2c_256_pairs", 32, 256, 64, 8, 256, FP8, "zipf"),
+    ("fp8_skinny_48_pairs", 6, 256, 64, 8, 256, FP8, "uniform"),
+    ("bf16_skinny_96_pairs", 12, 256, 128, 8, 256, BF16, "uniform"),
+    ("fp8_skinny_256_pairs", 32, 256, 64, 8, 256, FP8, "zipf"),
     ("bf16_skinny_t100", 100, 256, 16, 2, 256, BF16, "uniform"),
     ("bf16_skinny_t200", 200, 256, 32, 2, 128, BF16, "uniform"),
     # many pairs per expert: the 128-position tiled GEMMs (several tiles per
