@@ -268,7 +268,7 @@ __device__ __forceinline__ void run_mainloop(int mt, const char* const* a_rows,
       return;
     }
   }
-  if constexpr (BM / 2 >= 32 * WN) {
+  if constexpr (BM / 2 >= 32 * WN || BM / 2 == 16 * WN) {
     if (mt <= BM / 2) {
       tile_mainloop<MODE, BM / 2, WN, PD, BM / 16>(a_rows, b_rows, n_stages, lds, acc);
       return;
