@@ -42,7 +42,7 @@ inline long max_tiles_for(long n_pairs, int E, int bm) {
 // Offsets of the workspace regions for one shape.
 struct Layout {
   size_t ctrl, ids, wts, counts, offsets, sorted, inv, tiles, tiles_big, chunk_counts, chunk_base,
-      rank, xq, hq, h, y, logits, rtiles, total;
+      rank, xpart, xq, hq, h, y, logits, rtiles, total;
   long max_tiles, max_tiles_big, max_rtiles;
 };
 
@@ -92,6 +92,7 @@ Layout layout_for(const moe_shape& s) {
   L.chunk_base = take(n_chunks * s.E * 4);
   L.rank = take(np * 4);
   const bool fp8 = s.wdtype == MOE_FP8_E4M3;
+  L.xpart = take(fp8 ? kXParts * 4 : 0);
   L.xq = take(fp8 ? (size_t)s.T * s.H : 0);
   L.hq = take(fp8 ? (size_t)np * s.I : 0);
   L.h = take((size_t)np * s.I * act_bytes(s.wdtype));
@@ -530,26 +531,28 @@ int fused_impl(const moe_shape* s, const void* x, const float* logits, const voi
                             xq, st)))
       return rc;
   } else {
+    // FP8: the quantisation of x rides along in extra blocks of the gating
+    // launch (partial maxima of |x|) and of the grouping launch (amax(x) and
+    // the codes), beside their latency-bound work
+    const XWork xw{reinterpret_cast<const uint16_t*>(x), (long)T * H / 8, at<float>(ws, L.xpart),
+                   ctrl, xq};
+    const XWork* xwp = fp8 ? &xw : nullptr;
     // zeroes the control block
     MOE_TRY(launch_topk_gating(logits, T, E, k, s->renormalize, ids, wts,
-                               reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st));
+                               reinterpret_cast<uint32_t*>(ctrl), sizeof(Ctrl) / 4, st, xwp));
     MOE_TRY(mark(1));
     int32_t* nt = big ? &ctrl->num_tiles_big : &ctrl->num_tiles;
     if (grouping == Grouping::kChunked) {
       MOE_TRY(launch_chunk_sort(ids, T * k, E, counts, offsets, sorted, inv, bm, tl, nt,
                                 at<int32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.chunk_base),
-                                at<int32_t>(ws, L.rank), st));
+                                at<int32_t>(ws, L.rank), st, xwp));
       MOE_TRY(mark(2));
     } else {
-      MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st));
+      MOE_TRY(launch_align_sort(ids, T, k, E, counts, offsets, sorted, inv, st, xwp));
       MOE_TRY(mark(2));
       MOE_TRY(launch_build_tiles(offsets, E, bm, tl, nt, st));
     }
     MOE_TRY(mark(3));
-    if (fp8 &&
-        (rc = enqueue_quant(reinterpret_cast<const uint16_t*>(x), (long)T * H, &ctrl->amax_x_bits,
-                            xq, st)))
-      return rc;
   }
   if (big)
     MOE_TRY(launch_w13_tiles(s->wdtype, tiles_bm(*s), bx, w13, w13_scale, sorted, tiles_big,

@@ -137,13 +137,32 @@ inline void launch_on(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t
     kern<<<grid, block, 0, st>>>(static_cast<KArgs>(args)...);
 }
 
+// FP8 quantisation of x carried by extra blocks of the gating and grouping
+// launches of the many-pair path, next to their latency-bound work: the
+// gating launch's extra blocks each write the max |x| of their slice to
+// part[b] (no atomics, so nothing waits for the zeroed control block); the
+// grouping launch's extra blocks each reduce the kXParts partials, the first
+// writes amax(x) to ctrl->amax_x_bits, and all encode their slice of x.
+constexpr int kXParts = 256;    // partial-max blocks
+constexpr int kXQuantBlocks = 256;  // encoding blocks
+struct XWork {
+  const uint16_t* x;  // bf16, 8 * n8 values, 16-byte aligned
+  long n8;
+  float* part;        // kXParts floats of workspace
+  Ctrl* ctrl;
+  uint8_t* xq;        // e4m3 codes
+};
+
 // --------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All work goes to `st`.
+// With xw, the gating launch also writes the partial maxima of |x| and the
+// grouping launch (align sort or chunk sort) encodes x.
 hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
-                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st);
+                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st,
+                              const XWork* xw = nullptr);
 hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
-                             hipStream_t st);
+                             hipStream_t st, const XWork* xw = nullptr);
 // Gating, grouping, tile list and (xq != nullptr) FP8 quantisation of x in
 // one block, for T*k <= kRouteSmallMax; inv_perm may be null.  With wg (bf16
 // router weights [E,H], T*E <= kFusedRouterMaxTE) the logits are computed in
@@ -163,7 +182,7 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
 hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
                              int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
-                             int32_t* rank, hipStream_t st);
+                             int32_t* rank, hipStream_t st, const XWork* xw = nullptr);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
                               int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);

@@ -187,12 +187,83 @@ __device__ __forceinline__ void gate_token(const float* __restrict__ row, int E,
   }
 }
 
+// ------------------------------------------------- x work of extra blocks
+// Block b of nb (any block size up to 1024): max |x| over its grid-stride
+// slice into xw.part[b], four 16-byte loads in flight per thread.
+__device__ __forceinline__ void x_amax_part(const XWork& xw, int b, int nb) {
+  __shared__ float red[16];
+  const i32x4* s4 = reinterpret_cast<const i32x4*>(xw.x);
+  const long stride = (long)nb * blockDim.x;
+  float m = 0.f;
+  for (long i0 = (long)b * blockDim.x + threadIdx.x; i0 < xw.n8; i0 += 4 * stride) {
+    i32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      v[u] = i < xw.n8 ? s4[i] : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t w = (uint32_t)v[u][q];
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(w & 0xffffu))));
+        m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(w >> 16))));
+      }
+  }
+  m = wave_max(m);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = red[0];
+    for (int i = 1; i < (int)(blockDim.x / kWave); i++) a = fmaxf(a, red[i]);
+    xw.part[b] = a;
+  }
+}
+
+// Block b of nb: amax(x) from the kXParts partials (block 0 stores it in
+// the control block), then the e4m3 codes of its grid-stride slice (the
+// rule of quant_e4m3_kernel: codes of fl32(x * fl32(448 / amax))).
+__device__ __forceinline__ void x_quant_part(const XWork& xw, int b, int nb) {
+  __shared__ float red[16];
+  float a = 0.f;
+  for (int i = threadIdx.x; i < kXParts; i += blockDim.x) a = fmaxf(a, xw.part[i]);
+  a = wave_max(a);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = a;
+  __syncthreads();
+  a = red[0];
+  for (int i = 1; i < (int)(blockDim.x / kWave); i++) a = fmaxf(a, red[i]);
+  if (b == 0 && threadIdx.x == 0) xw.ctrl->amax_x_bits = __float_as_uint(a);
+  const float r = a > 0.f ? 448.0f / a : 1.0f;
+  const i32x4* s4 = reinterpret_cast<const i32x4*>(xw.x);
+  uint2* d2 = reinterpret_cast<uint2*>(xw.xq);
+  const long stride = (long)nb * blockDim.x;
+  for (long i0 = (long)b * blockDim.x + threadIdx.x; i0 < xw.n8; i0 += 4 * stride) {
+    i32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      v[u] = i < xw.n8 ? s4[i] : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const long i = i0 + u * stride;
+      if (i < xw.n8) d2[i] = bf16x8_to_e4m3x8(v[u], r);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int renorm,
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ wts,
-                                                          uint32_t* zero_words, int n_zero) {
+                                                          uint32_t* zero_words, int n_zero,
+                                                          int gate_blocks, XWork xw) {
   __shared__ __attribute__((aligned(16))) float gscr[4][kGateScratch];
+  if ((int)blockIdx.x >= gate_blocks) {  // block-uniform
+    x_amax_part(xw, blockIdx.x - gate_blocks, kXParts);
+    return;
+  }
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero_words[i] = 0u;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -202,11 +273,13 @@ __global__ __launch_bounds__(256) void topk_gating_kernel(const float* __restric
 }
 
 hipError_t launch_topk_gating(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
-                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st) {
+                              float* w, uint32_t* zero_words, int n_zero, hipStream_t st,
+                              const XWork* xw) {
   const int tokens_per_block = 4;
   int grid = (T + tokens_per_block - 1) / tokens_per_block;
   if (grid < 1) grid = 1;
-  topk_gating_kernel<<<grid, 256, 0, st>>>(logits, T, E, k, renorm, ids, w, zero_words, n_zero);
+  topk_gating_kernel<<<grid + (xw ? kXParts : 0), 256, 0, st>>>(
+      logits, T, E, k, renorm, ids, w, zero_words, n_zero, grid, xw ? *xw : XWork{});
   return hipGetLastError();
 }
 
@@ -245,9 +318,14 @@ __global__ __launch_bounds__(256) void align_sort_kernel(const int32_t* __restri
                                                          int E, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted_ids,
-                                                         int32_t* __restrict__ inv_perm) {
+                                                         int32_t* __restrict__ inv_perm,
+                                                         XWork xw) {
   __shared__ int hist[1024];
   __shared__ int tmp[4];
+  if ((int)blockIdx.x >= E) {  // block-uniform: the x encoding blocks
+    x_quant_part(xw, blockIdx.x - E, kXQuantBlocks);
+    return;
+  }
   const int e = blockIdx.x;
   for (int i = threadIdx.x; i < E; i += 256) hist[i] = 0;
   __syncthreads();
@@ -308,8 +386,9 @@ __global__ __launch_bounds__(256) void align_sort_kernel(const int32_t* __restri
 
 hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* sorted_ids, int32_t* inv_perm,
-                             hipStream_t st) {
-  align_sort_kernel<<<E, 256, 0, st>>>(ids, T * k, E, counts, offsets, sorted_ids, inv_perm);
+                             hipStream_t st, const XWork* xw) {
+  align_sort_kernel<<<E + (xw ? kXQuantBlocks : 0), 256, 0, st>>>(
+      ids, T * k, E, counts, offsets, sorted_ids, inv_perm, xw ? *xw : XWork{});
   return hipGetLastError();
 }
 
@@ -705,9 +784,14 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
 // order as the one-kernel grouping.
 __global__ __launch_bounds__(1024) void chunk_rank_kernel(const int32_t* __restrict__ ids, int n,
                                                           int E, int32_t* __restrict__ chunk_counts,
-                                                          int32_t* __restrict__ rank) {
+                                                          int32_t* __restrict__ rank,
+                                                          int n_chunks, XWork xw) {
   __shared__ __attribute__((aligned(16))) int s_ids[kSortChunk];
   __shared__ int hist[1024];
+  if ((int)blockIdx.x >= n_chunks) {  // block-uniform: the x encoding blocks
+    x_quant_part(xw, blockIdx.x - n_chunks, kXQuantBlocks);
+    return;
+  }
   const int t = threadIdx.x, c = blockIdx.x;
   const int f0 = c * kSortChunk, m = min(kSortChunk, n - f0);
   hist[t] = 0;
@@ -807,9 +891,10 @@ __global__ __launch_bounds__(1024) void chunk_scatter_kernel(const int32_t* __re
 hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
                              int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
-                             int32_t* rank, hipStream_t st) {
+                             int32_t* rank, hipStream_t st, const XWork* xw) {
   const int n_chunks = (n + kSortChunk - 1) / kSortChunk;
-  chunk_rank_kernel<<<n_chunks, 1024, 0, st>>>(ids, n, E, chunk_counts, rank);
+  chunk_rank_kernel<<<n_chunks + (xw ? kXQuantBlocks : 0), 1024, 0, st>>>(
+      ids, n, E, chunk_counts, rank, n_chunks, xw ? *xw : XWork{});
   chunk_scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, n_chunks, E, n, counts, offsets, base, bm,
                                         tiles, num_tiles);
   chunk_scatter_kernel<<<(n + 1023) / 1024, 1024, 0, st>>>(ids, rank, base, n, E, sorted_ids,
