@@ -67,6 +67,9 @@ CASES = [
     ("fp8_tiles_heavy_zipf", 3000, 256, 8, 2, 256, FP8, "zipf"),
     ("bf16_tiles_heavy", 2900, 256, 8, 1, 384, BF16, "uniform"),
     ("fp8_tiles_heavy_h384", 1100, 384, 4, 1, 256, FP8, "uniform"),
+    # 128-position tiles whose rows are one 128-byte K stage long (H = I =
+    # 128 in FP8): every prefetch index is clamped to that stage
+    ("fp8_tiles128_one_stage", 600, 128, 4, 2, 128, FP8, "uniform"),
     # 16 <= mean pairs per expert < 64: 64-position tiles, some experts spill
     # into a second tile
     ("fp8_tiles64_ragged", 250, 384, 8, 2, 384, FP8, "uniform"),
