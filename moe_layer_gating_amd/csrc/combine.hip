@@ -5,7 +5,10 @@
 // agentic-affairs.com, "Triton improves the FP8 execution path").
 //   out[t][m] = sum_{j<k} w[t][j] * y[inv_perm[t*k+j]][m]
 // summed in fp32 in slot order j = 0..k-1 and rounded once; each output row
-// is written exactly once, by one thread per 8 consecutive features.  y is
+// is written exactly once, by one thread per 8 consecutive features, in
+// blocks of 128 threads (a 7168-feature row is 7 whole blocks; with blocks
+// of 256 the fourth block of every row was half idle, and the prefill
+// aggregation ran 4% slower).  y is
 // fp32, or bf16 (YB: the FP8 fused path of many-token layers: one 16-byte
 // load per slot), widened exactly before the sum.
 #include "moe_common.h"
@@ -13,7 +16,7 @@
 namespace moe {
 
 template <int MODE, bool YB>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
+__global__ __launch_bounds__(128) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const float* __restrict__ w, int T, int H,
                                                       int k, int blocks_per_row,
@@ -80,16 +83,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 hipError_t launch_combine(int mode, const void* y, bool y_bf16, const int32_t* inv_perm,
                           const float* w, int T, int H, int k, void* out, hipStream_t st) {
-  const int bpr = (H / 8 + 255) / 256;
+  const int bpr = (H / 8 + 127) / 128;
   const long grid = (long)bpr * T;
   if (grid <= 0) return hipSuccess;
   if (mode == MOE_F32 && y_bf16) return hipErrorInvalidValue;
   if (mode == MOE_F32)
-    combine_kernel<MOE_F32, false><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+    combine_kernel<MOE_F32, false><<<grid, 128, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
   else if (y_bf16)
-    combine_kernel<MOE_BF16, true><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+    combine_kernel<MOE_BF16, true><<<grid, 128, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
   else
-    combine_kernel<MOE_BF16, false><<<grid, 256, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
+    combine_kernel<MOE_BF16, false><<<grid, 128, 0, st>>>(y, inv_perm, w, T, H, k, bpr, out);
   return hipGetLastError();
 }
 
