@@ -776,7 +776,9 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
 // in three launches instead of one block per expert scanning every pair:
 //   chunk_rank_kernel : per chunk, the expert histogram and each pair's rank
 //                       among the earlier pairs of its chunk on the same
-//                       expert (broadcast LDS reads, no atomics decide it);
+//                       expert (ballots match the lanes of a wave holding
+//                       the same expert; per-wave counts are summed over
+//                       the earlier waves; no atomics decide it);
 //   chunk_scan_kernel : expert totals, offsets, and every chunk's starting
 //                       position inside each expert's group; the tile list;
 //   chunk_scatter_kernel : position = chunk base of the expert + rank.
@@ -786,34 +788,44 @@ __global__ __launch_bounds__(1024) void chunk_rank_kernel(const int32_t* __restr
                                                           int E, int32_t* __restrict__ chunk_counts,
                                                           int32_t* __restrict__ rank,
                                                           int n_chunks, XWork xw) {
-  __shared__ __attribute__((aligned(16))) int s_ids[kSortChunk];
-  __shared__ int hist[1024];
+  constexpr int NW = kSortChunk / kWave;  // waves of the block, one pair per thread
+  __shared__ int whist[NW][1024];         // pairs of wave w on expert e
   if ((int)blockIdx.x >= n_chunks) {  // block-uniform: the x encoding blocks
     x_quant_part(xw, blockIdx.x - n_chunks, kXQuantBlocks);
     return;
   }
-  const int t = threadIdx.x, c = blockIdx.x;
+  const int t = threadIdx.x, c = blockIdx.x, w = t / kWave, lane = lane_id();
   const int f0 = c * kSortChunk, m = min(kSortChunk, n - f0);
-  hist[t] = 0;
-  s_ids[t] = t < m ? ids[f0 + t] : -1;  // kSortChunk == blockDim.x
+  for (int i = t; i < NW * E; i += blockDim.x) whist[i / E][i % E] = 0;
+  const bool valid = t < m;
+  const int e = valid ? ids[f0 + t] : 0;
+  // lanes of this wave holding the same expert: one ballot per bit of the
+  // expert index (E <= 1024: ten bits), narrowed to the valid lanes
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 10; b++) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(bit);
+    same &= bit ? ones : ~ones;
+  }
+  const int intra = __popcll(same & ((1ull << lane) - 1));  // earlier lanes, same expert
+  __syncthreads();  // whist zeroed
+  // the first lane of each expert group records the group's size (one
+  // writer per (wave, expert): no atomics)
+  if (valid && intra == 0) whist[w][e] = __popcll(same);
   __syncthreads();
-  if (t < m) {
-    const int e = s_ids[t];
-    atomicAdd(&hist[e], 1);
-    // earlier pairs of this chunk on the same expert: 16-byte LDS reads that
-    // every lane of a wave takes from the same address (broadcast)
-    int r = 0;
-    const int4* s4 = reinterpret_cast<const int4*>(s_ids);
-    const int full = t >> 2;
-    for (int j = 0; j < full; j++) {
-      const int4 v = s4[j];
-      r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-    }
-    for (int j = full * 4; j < t; j++) r += (s_ids[j] == e);
+  // rank = pairs of earlier waves on the expert + earlier lanes of this wave
+  if (valid) {
+    int r = intra;
+    for (int i = 0; i < w; i++) r += whist[i][e];
     rank[f0 + t] = r;
   }
-  __syncthreads();
-  if (t < E) chunk_counts[(size_t)c * E + t] = hist[t];
+  for (int ee = t; ee < E; ee += blockDim.x) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < NW; i++) s += whist[i][ee];
+    chunk_counts[(size_t)c * E + ee] = s;
+  }
 }
 
 __global__ __launch_bounds__(1024) void chunk_scan_kernel(
