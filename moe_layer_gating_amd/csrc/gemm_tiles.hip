@@ -58,7 +58,10 @@
 // [x n / 8, (x + 1) n / 8), each with all its row blocks: a tile's token rows
 // are then fetched into one L2 instead of eight (the mixed layer's down
 // projection ran 3.6-6% faster; with the 128-position tiles of the prefill
-// layers such orders were slower).
+// layers such orders were slower).  The 128-position down projection of a
+// Zipf-skewed prefill batch takes its tiles in the spread order the grouping
+// writes (full tiles evenly among the partial ones); the kernels only
+// follow the list they are given.
 #include "moe_common.h"
 
 namespace moe {

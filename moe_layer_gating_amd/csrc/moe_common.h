@@ -179,10 +179,13 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
 // Grouping of n pairs in chunks of kSortChunk plus the tile list of <= bm
 // positions (three launches).  Scratch: chunk_counts and base hold
 // ceil(n / kSortChunk) * E ints each, rank n ints.
+// With tiles_spread, the chunked grouping also writes the tile list in the
+// down projection's launch order (full tiles spread evenly among the others).
 hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
                              int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
-                             int32_t* rank, hipStream_t st, const XWork* xw = nullptr);
+                             int32_t* rank, hipStream_t st, const XWork* xw = nullptr,
+                             Tile* tiles_spread = nullptr);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, Tile* tiles,
                               int32_t* num_tiles, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);

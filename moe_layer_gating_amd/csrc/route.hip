@@ -780,7 +780,9 @@ hipError_t launch_route_small(const float* logits, int T, int E, int k, int reno
 //                       the same expert; per-wave counts are summed over
 //                       the earlier waves; no atomics decide it);
 //   chunk_scan_kernel : expert totals, offsets, and every chunk's starting
-//                       position inside each expert's group; the tile list;
+//                       position inside each expert's group; the tile list
+//                       (and, when asked, the same tiles in the down
+//                       projection's launch order);
 //   chunk_scatter_kernel : position = chunk base of the expert + rank.
 // Positions are therefore ordered by (expert, pair index), the same stable
 // order as the one-kernel grouping.
@@ -828,10 +830,58 @@ __global__ __launch_bounds__(1024) void chunk_rank_kernel(const int32_t* __restr
   }
 }
 
+// The spread order of n tiles, F of them full: full tile a (counted in list
+// order) goes to position a * n / F, and the partial tiles fill the positions
+// left, in list order: partial tile b takes the smallest p at which the count
+// of free positions up to p, p + 1 - ceil((p + 1) F / n), reaches b + 1.  A
+// permutation of 0 .. n-1.
+// U is the integer type of the products: 32-bit while n * n fits (a 64-bit
+// division is a long software routine, and one thread per expert places all
+// of its expert's tiles).
+template <typename U>
+__device__ __forceinline__ int partial_position(int rank, int n, int F) {
+  int lo = rank, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const U q = (U)(mid + 1);
+    if (q - (q * (U)F + (U)(n - 1)) / (U)n >= (U)(rank + 1))
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+// Writes one expert's tiles (nfull full ones, then at most one partial one,
+// the first full one of list rank a0, the partial one of rank b) at their
+// spread positions; successive full positions a * n / F advance by n / F
+// with a carry, so the loop divides nothing.
+template <typename U>
+__device__ __forceinline__ void place_spread(Tile tl, int bm, int cnt, int nfull, int a0, int b,
+                                             int n, int F, Tile* __restrict__ out) {
+  if (nfull > 0) {
+    const U step_q = (U)n / (U)F, step_r = (U)n % (U)F;
+    U q = (U)a0 * (U)n / (U)F, rem = (U)a0 * (U)n % (U)F;
+    for (int i = 0; i < nfull; i++) {
+      tl.p0 = tl.p0 + (i ? bm : 0);
+      tl.mt = bm;
+      out[(int)q] = tl;
+      q += step_q;
+      rem += step_r;
+      if (rem >= (U)F) rem -= (U)F, q += 1;
+    }
+  }
+  if (cnt > nfull * bm) {
+    tl.p0 = tl.p0 + (nfull ? bm : 0);
+    tl.mt = cnt - nfull * bm;
+    out[partial_position<U>(b, n, F)] = tl;
+  }
+}
+
 __global__ __launch_bounds__(1024) void chunk_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int n_chunks, int E, int n,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ base,
-    int bm, Tile* __restrict__ tiles, int32_t* num_tiles) {
+    int bm, Tile* __restrict__ tiles, int32_t* num_tiles, Tile* __restrict__ tiles_spread) {
   __shared__ int tmp[16];
   const int t = threadIdx.x;
   int cnt = 0;
@@ -850,9 +900,12 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(
     for (; c < n_chunks; c++) cnt += chunk_counts[(size_t)c * E + t];
   }
   const int nt = (cnt + bm - 1) / bm;
-  int total_pairs, total_tiles;
+  const int nfull = cnt / bm;  // tiles of exactly bm positions, listed first
+  int total_pairs, total_tiles, total_full = 0;
   const int pre = block_exclusive_scan_1024(cnt, tmp, &total_pairs);
   const int tpre = block_exclusive_scan_1024(nt, tmp, &total_tiles);
+  int fpre = 0;
+  if (tiles_spread) fpre = block_exclusive_scan_1024(nfull, tmp, &total_full);
   if (t < E) {
     counts[t] = cnt;
     offsets[t] = pre;
@@ -880,6 +933,17 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(
       tl.pad = 0;
       tiles[tpre + i] = tl;
     }
+    if (tiles_spread && nt > 0) {
+      // list ranks: this expert's full tiles follow fpre full ones, its
+      // partial tile follows the tpre - fpre partial ones before it
+      const Tile first = {t, pre, 0, 0};
+      if (total_tiles <= 65535)
+        place_spread<uint32_t>(first, bm, cnt, nfull, fpre, tpre - fpre, total_tiles, total_full,
+                               tiles_spread);
+      else
+        place_spread<uint64_t>(first, bm, cnt, nfull, fpre, tpre - fpre, total_tiles, total_full,
+                               tiles_spread);
+    }
   }
   if (t == 0) {
     offsets[E] = n;
@@ -903,12 +967,13 @@ __global__ __launch_bounds__(1024) void chunk_scatter_kernel(const int32_t* __re
 hipError_t launch_chunk_sort(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_ids, int32_t* inv_perm, int bm, Tile* tiles,
                              int32_t* num_tiles, int32_t* chunk_counts, int32_t* base,
-                             int32_t* rank, hipStream_t st, const XWork* xw) {
+                             int32_t* rank, hipStream_t st, const XWork* xw,
+                             Tile* tiles_spread) {
   const int n_chunks = (n + kSortChunk - 1) / kSortChunk;
   chunk_rank_kernel<<<n_chunks + (xw ? kXQuantBlocks : 0), 1024, 0, st>>>(
       ids, n, E, chunk_counts, rank, n_chunks, xw ? *xw : XWork{});
   chunk_scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, n_chunks, E, n, counts, offsets, base, bm,
-                                        tiles, num_tiles);
+                                        tiles, num_tiles, tiles_spread);
   chunk_scatter_kernel<<<(n + 1023) / 1024, 1024, 0, st>>>(ids, rank, base, n, E, sorted_ids,
                                                            inv_perm);
   return hipGetLastError();

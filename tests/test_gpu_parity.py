@@ -76,6 +76,10 @@ CASES = [
     # 8192 pairs or more: the grouping runs as a chunked counting sort (ragged
     # last chunk) inside the fused entry point
     ("fp8_tiles_chunked_sort", 1100, 256, 16, 8, 256, FP8, "zipf"),
+    # chunked grouping with 128-position tiles and under 256 pairs per
+    # expert: the down projection takes the spread tile order (full tiles
+    # evenly among the partial ones of the skewed experts)
+    ("fp8_tiles_spread_zipf", 1200, 256, 64, 8, 256, FP8, "zipf"),
     ("bf16_tiles_chunked_sort", 4200, 128, 64, 2, 128, BF16, "uniform"),
     # the interface's largest expert count and top-k (E = 1024, k = 16): 256
     # pairs, the most the one-block front kernel takes; 272 pairs, just past
